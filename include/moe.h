@@ -1,0 +1,169 @@
+/*
+ * moe.h -- C ABI of libmoe: the MoE-layer hot path on one GPU's share of the
+ * tokens, hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * The calls follow the problem the pages pose:
+ *  - route each token to k of E experts
+ *      (Zyphra correlated expert placement page, English abstract);
+ *  - count the expert pairs that one token activates together
+ *      (Cobalt page, English abstract);
+ *  - place E experts on G expert-parallel ranks and dispatch each token to
+ *    each rank once, grouped by expert
+ *      (Zyphra page, English abstract: correlated placement and the
+ *       once-per-GPU dispatcher);
+ *  - run the expert networks on the dispatched rows (same page);
+ *  - combine the expert results back into token order (same page).
+ *
+ * Conventions shared by every call
+ *  - Every pointer argument is DEVICE memory owned by the caller, except
+ *    where a comment says otherwise. The library allocates nothing and keeps
+ *    no state besides a per-device property cache.
+ *  - Matrices are row-major and densely packed (row stride = row length).
+ *  - bf16 tensors hold IEEE bfloat16 bit patterns (2 bytes per element).
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and only
+ *    enqueues work; it never synchronises the host. Outputs must not alias
+ *    inputs. Calls on disjoint buffers may run concurrently.
+ *  - Argument errors are detected on the host before anything is enqueued
+ *    and return MOE_ERR_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE with
+ *    the outputs untouched. A failed kernel launch returns MOE_ERR_DEVICE.
+ *  - Out-of-range VALUES inside device arrays (an expert id outside [0,E), a
+ *    rank outside [0,G), NaN logits) cannot be seen by the host and give
+ *    unspecified (but in-bounds) results.
+ *  - Limits: 0 <= T, 1 <= k <= 16, k <= E <= 256, 1 <= G <= 32,
+ *    T*k < 2^31. For the expert FFN d and F must be multiples of 64.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,          /* a size, pointer or enum is invalid        */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid, but outside what the kernels cover */
+    MOE_ERR_WORKSPACE = 3,    /* workspace missing or too small            */
+    MOE_ERR_DEVICE = 4        /* a HIP call or kernel launch failed        */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Version of this ABI (MOE_ABI_VERSION of the build). */
+int moe_abi_version(void);
+
+/* Static string naming a status code. */
+const char* moe_status_str(int status);
+
+/*
+ * Top-k routing (Zyphra page, English abstract: each token goes to k of the
+ * E experts).
+ *  logits   [T,E] fp32: router logits of T tokens.
+ *  topk_idx [T,k] int32 out: chosen experts, by descending logit; equal
+ *           logits go to the lower expert index (-0 equals +0).
+ *  gates    [T,k] fp32 out: softmax over the k chosen logits (sums to 1).
+ *  n_groups, topk_groups: group-limited routing. The E experts form n_groups
+ *           contiguous groups of E/n_groups; a group's score is its largest
+ *           logit; only the topk_groups best groups (ties -> lower group)
+ *           stay eligible. n_groups = topk_groups = 1 is plain top-k.
+ *           Requires n_groups | E, topk_groups <= n_groups and
+ *           topk_groups * E / n_groups >= k.
+ *  -inf logits are allowed as long as each token has k finite eligible ones.
+ */
+moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                     int32_t n_groups, int32_t topk_groups,
+                     int32_t* topk_idx, float* gates, hipStream_t stream);
+
+/*
+ * Expert co-activation histogram (Cobalt page, English abstract: pairs of
+ * experts that a single token activates together).
+ *  topk_idx [T,k] int32: routing result (k distinct experts per token).
+ *  coact    [E,E] int32 in/out: ACCUMULATES, for every token and every
+ *           ordered pair (a,b), a != b, of its experts, coact[a][b] += 1.
+ *           The matrix stays symmetric and its diagonal untouched; zero it
+ *           first for a fresh count.
+ */
+moe_status moe_coact_hist(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                          int32_t* coact, hipStream_t stream);
+
+/* Bytes of device workspace moe_dispatch_layout needs (host call, no GPU). */
+size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t G);
+
+/*
+ * Dispatch layout and dispatch rows (Zyphra page, English abstract: experts
+ * placed on GPUs, a dispatcher that sends each token to each GPU once).
+ *  topk_idx  [T,k] int32: routing result.
+ *  place     [E] int32: rank of each expert, in [0,G) (a partition).
+ *  x         [T,d] activations (dt), or NULL to build only the indices.
+ * Outputs (sized for the upper bound T*k where noted):
+ *  rank_mask [T] uint32: bit g set iff a chosen expert of t sits on rank g.
+ *  rank_off  [G+1] int32: row offsets per rank; R = rank_off[G] rows.
+ *  disp_token[T*k] int32: first R entries: for each rank in order, the
+ *            tokens sent to it in ascending order (one row per distinct
+ *            (token, rank) pair).
+ *  expert_off[E+1] int32: slot offsets per expert.
+ *  perm_row  [T*k] int32: slot s (experts ascending, tokens ascending within
+ *            an expert) reads dispatched row perm_row[s].
+ *  slot_of   [T*k] int32: slot of (token t, choice j) at index t*k+j.
+ *  x_disp    [T*k,d] (dt): rows 0..R-1 get x[disp_token[r]]; ignored if
+ *            x is NULL.
+ *  workspace: device scratch of at least moe_dispatch_workspace_bytes().
+ * R stays on the device; nothing is copied back to the host.
+ */
+moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                               const int32_t* place, int32_t G,
+                               const void* x, int32_t d, moe_dtype dt,
+                               uint32_t* rank_mask, int32_t* rank_off, int32_t* disp_token,
+                               int32_t* expert_off, int32_t* perm_row, int32_t* slot_of,
+                               void* x_disp, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Expert networks, first half: for every slot s of expert e (expert_off),
+ *   a = x_disp[perm_row[s]],  u = W_gate[e] a,  v = W_up[e] a,
+ *   h[s] = silu(u) * v,       silu(u) = u / (1 + exp(-u)).
+ * The pages only say "expert networks"; this is a bias-free SwiGLU MLP.
+ *  x_disp [*,d] (dt), w_gate / w_up [E,F,d] (dt, output index first),
+ *  h [T*k,F] (dt) out; rows expert_off[E]..T*k-1 are not written.
+ * bf16: bf16 MFMA with fp32 accumulation, h rounded to bf16 (RNE).
+ */
+moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm_row,
+                              const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
+                              int32_t d, int32_t F, const void* w_gate, const void* w_up,
+                              moe_dtype dt, void* h, hipStream_t stream);
+
+/*
+ * Expert networks, second half: y[s] = W_down[e] h[s] for every slot s of
+ * expert e.  h [T*k,F] (dt), w_down [E,d,F] (dt), y [T*k,d] (dt) out.
+ */
+moe_status moe_expert_down(const void* h, const int32_t* expert_off, int32_t T, int32_t E,
+                           int32_t k, int32_t d, int32_t F, const void* w_down, moe_dtype dt,
+                           void* y, hipStream_t stream);
+
+/* Both halves in order: moe_expert_gate_up then moe_expert_down. */
+moe_status moe_grouped_ffn(const void* x_disp, const int32_t* perm_row, const int32_t* expert_off,
+                           int32_t T, int32_t E, int32_t k, int32_t d, int32_t F,
+                           const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
+                           void* h, void* y, hipStream_t stream);
+
+/*
+ * Combine back to token order (Zyphra page, English abstract: the expert
+ * results are combined): out[t] = sum_j gates[t,j] * y[slot_of[t*k+j]],
+ * accumulated in fp32 in j order, stored in dt (bf16: RNE).
+ *  y [T*k,d] (dt), slot_of [T*k], gates [T,k] fp32, out [T,d] (dt) out.
+ */
+moe_status moe_combine(const void* y, const int32_t* slot_of, const float* gates,
+                       int32_t T, int32_t k, int32_t d, moe_dtype dt, void* out,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

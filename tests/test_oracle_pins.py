@@ -1,0 +1,406 @@
+"""Pins of the fp64 reference against things other than itself.
+
+Each step of the reference is checked against brute force on tiny inputs, an
+independent library routine, a closed form or an invariant that the method
+fixes, chosen so that a dropped term, a wrong sign, a wrong index or a
+transposed operand in the reference fails at least one test.
+"""
+import itertools
+import math
+import random
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+from routing_dispatch_expert_top_amd import synth
+
+
+# ------------------------------------------------------------------ helpers
+
+def precedes(la, ia, lb, ib):
+    return la > lb or (la == lb and ia < ib)
+
+
+def brute_route(row, k, n_groups=1, topk_groups=1):
+    """Selected experts characterised as the unique k-subset whose members all
+    precede every eligible non-member; found by enumerating subsets."""
+    E = len(row)
+    gsz = E // n_groups
+    groups = list(range(n_groups))
+    if n_groups > 1:
+        score = [max(row[m * gsz:(m + 1) * gsz]) for m in groups]
+        good = []
+        for S in itertools.combinations(groups, topk_groups):
+            if all(precedes(score[a], a, score[b], b) for a in S for b in groups if b not in S):
+                good.append(S)
+        assert len(good) == 1
+        eligible = [e for e in range(E) if e // gsz in good[0]]
+    else:
+        eligible = list(range(E))
+    good = []
+    for S in itertools.combinations(eligible, k):
+        if all(precedes(row[a], a, row[b], b) for a in S for b in eligible if b not in S):
+            good.append(S)
+    assert len(good) == 1
+    # order inside the chosen set: count of members preceding each one
+    S = good[0]
+    order = sorted(S, key=lambda a: sum(precedes(row[b], b, row[a], a) for b in S))
+    return order
+
+
+def lexsort_route(L, k, n_groups=1, topk_groups=1):
+    """Top-k with numpy's lexsort: key (ineligible, -logit, index)."""
+    T, E = L.shape
+    inel = np.zeros((T, E), np.int8)
+    if n_groups > 1:
+        gsz = E // n_groups
+        gs = L.reshape(T, n_groups, gsz).max(-1)
+        gidx = np.broadcast_to(np.arange(n_groups), gs.shape)
+        gord = np.lexsort((gidx, -gs), axis=1)[:, :topk_groups]
+        keep = np.zeros((T, n_groups), bool)
+        np.put_along_axis(keep, gord, True, axis=1)
+        inel = (~np.repeat(keep, gsz, axis=1)).astype(np.int8)
+    eidx = np.broadcast_to(np.arange(E), (T, E))
+    return np.lexsort((eidx, -L.astype(np.float64), inel), axis=1)[:, :k].astype(np.int32)
+
+
+def selection_matrix(idx, E):
+    T = idx.shape[0]
+    A = np.zeros((T, E), np.int64)
+    np.put_along_axis(A, idx.astype(np.int64), 1, axis=1)
+    return A
+
+
+# ------------------------------------------------------------------ route
+
+@pytest.mark.parametrize("seed", range(40))
+def test_route_brute_force_with_ties(orc, seed):
+    rnd = random.Random(seed)
+    E = rnd.choice([2, 3, 4, 6, 8])
+    k = rnd.randint(1, E)
+    T = rnd.randint(1, 12)
+    pool = [-1.0, -0.0, 0.0, 0.5, 1.0, 2.0, -np.inf]
+    L = np.array([[rnd.choice(pool) for _ in range(E)] for _ in range(T)], np.float32)
+    # at least k finite logits per token
+    L[:, :k] = np.where(np.isinf(L[:, :k]), 0.25, L[:, :k])
+    idx, g = orc.route(L, k)
+    for t in range(T):
+        row = [float(v) for v in L[t]]
+        assert list(idx[t]) == brute_route(row, k)
+        np.testing.assert_allclose(g[t], softmax(np.array(row)[idx[t]]), rtol=1e-13, atol=1e-300)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_route_group_limited_brute_force(orc, seed):
+    rnd = random.Random(1000 + seed)
+    n_groups, gsz = rnd.choice([(4, 2), (2, 4), (4, 1), (8, 1)])
+    E = n_groups * gsz
+    topk_groups = rnd.randint(1, n_groups)
+    k = rnd.randint(1, topk_groups * gsz)
+    T = rnd.randint(1, 10)
+    L = np.array([[rnd.choice([-1.0, 0.0, -0.0, 0.5, 1.5]) for _ in range(E)] for _ in range(T)],
+                 np.float32)
+    idx, _ = orc.route(L, k, n_groups, topk_groups)
+    for t in range(T):
+        assert list(idx[t]) == brute_route([float(v) for v in L[t]], k, n_groups, topk_groups)
+
+
+@pytest.mark.parametrize("wi", range(5))
+def test_route_vs_lexsort_on_workloads(orc, wi):
+    w = synth.workload(wi)
+    L = synth.logits(w)
+    idx, g = orc.route(L, w.k, w.n_groups, w.topk_groups)
+    assert np.array_equal(idx, lexsort_route(L, w.k, w.n_groups, w.topk_groups))
+    sel = np.take_along_axis(L.astype(np.float64), idx, axis=1)
+    np.testing.assert_allclose(g, softmax(sel, axis=1), rtol=1e-12)
+    np.testing.assert_allclose(g.sum(1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(np.diff(g, axis=1) <= 0)          # listed by descending logit
+
+
+def test_route_group_limited_properties(orc):
+    w = synth.workload(4)
+    L = synth.logits(w)[:2048]
+    idx, _ = orc.route(L, w.k, w.n_groups, w.topk_groups)
+    gsz = w.E // w.n_groups
+    gs = L.reshape(L.shape[0], w.n_groups, gsz).max(-1)
+    for t in range(L.shape[0]):
+        used = set(int(e) // gsz for e in idx[t])
+        assert len(used) <= w.topk_groups
+        chosen = np.argsort(-gs[t], kind="stable")[:w.topk_groups]
+        assert used <= set(int(c) for c in chosen)
+
+
+def test_route_k1_gate_is_one_and_two_way_logistic(orc):
+    rng = np.random.default_rng(5)
+    L = rng.standard_normal((300, 16)).astype(np.float32)
+    _, g1 = orc.route(L, 1)
+    assert np.all(g1 == 1.0)
+    idx2, g2 = orc.route(L, 2)
+    l = np.take_along_axis(L.astype(np.float64), idx2, axis=1)
+    np.testing.assert_allclose(g2[:, 0], expit(l[:, 0] - l[:, 1]), rtol=1e-13)
+    np.testing.assert_allclose(g2[:, 1], expit(l[:, 1] - l[:, 0]), rtol=1e-12)
+
+
+def test_route_rejects_bad_args(orc):
+    L = np.zeros((4, 8), np.float32)
+    # k > E; k < 1; groups do not divide E; topk_groups > n_groups;
+    # fewer than k eligible experts (5 > 2 groups x 2, and 2 > 1 group x 1)
+    for args in [(9, 1, 1), (0, 1, 1), (2, 3, 1), (2, 4, 5), (5, 4, 2), (2, 8, 1)]:
+        with pytest.raises(ValueError):
+            orc.route(L, *args)
+
+
+# ------------------------------------------------------------------ coact
+
+@pytest.mark.parametrize("wi", range(5))
+def test_coact_closed_form_and_invariants(orc, wi):
+    w = synth.workload(wi)
+    idx, _ = orc.route(synth.logits(w), w.k, w.n_groups, w.topk_groups)
+    C = orc.coact(idx, w.E)
+    A = selection_matrix(idx, w.E)
+    AtA = A.T @ A
+    assert np.array_equal(C, AtA - np.diag(np.diag(AtA)))
+    assert np.array_equal(C, C.T)
+    assert np.all(np.diag(C) == 0)
+    n_e = np.bincount(idx.ravel(), minlength=w.E)
+    assert np.array_equal(C.sum(1), (w.k - 1) * n_e)
+    assert C.sum() == w.T * w.k * (w.k - 1)
+
+
+def test_coact_tiny_brute(orc):
+    idx = np.array([[0, 1], [1, 0], [2, 3], [0, 3]], np.int32)
+    C = orc.coact(idx, 4)
+    want = np.zeros((4, 4), np.int64)
+    for a, b in [(0, 1), (1, 0), (1, 0), (0, 1), (2, 3), (3, 2), (0, 3), (3, 0)]:
+        want[a, b] += 1
+    assert np.array_equal(C, want)
+
+
+def test_coact_k1_is_zero(orc):
+    idx = np.arange(10, dtype=np.int32).reshape(10, 1) % 4
+    assert not orc.coact(idx, 4).any()
+
+
+# ------------------------------------------------------------------ layout
+
+def check_layout(lay, idx, place, G, E):
+    T, k = idx.shape
+    rank = place[idx]                                      # [T,k]
+    pairs = {(t, int(g)) for t in range(T) for g in rank[t]}
+    R = len(pairs)
+    assert lay["R"] == R <= T * k
+    # masks
+    for t in range(T):
+        assert int(lay["rank_mask"][t]) == sum(1 << g for g in set(int(v) for v in rank[t]))
+    # rank-major, token-ascending rows via lexsort of the (rank, token) set
+    pr = np.array(sorted(pairs, key=lambda p: (p[1], p[0])), np.int64).reshape(-1, 2)
+    assert np.array_equal(lay["disp_token"], pr[:, 0])
+    cnt = np.bincount(pr[:, 1], minlength=G)
+    assert np.array_equal(lay["rank_off"], np.concatenate([[0], np.cumsum(cnt)]))
+    # expert offsets and slot order via stable argsort
+    eoff = np.concatenate([[0], np.cumsum(np.bincount(idx.ravel(), minlength=E))])
+    assert np.array_equal(lay["expert_off"], eoff)
+    order = np.argsort(idx.ravel(), kind="stable")         # slot -> flat (t,j)
+    so = np.empty(T * k, np.int64)
+    so[order] = np.arange(T * k)
+    assert np.array_equal(lay["slot_of"], so)
+    assert np.array_equal(np.sort(lay["slot_of"]), np.arange(T * k))   # bijection
+    # each slot's row carries its token to its expert's rank
+    t_of_slot = order // k
+    e_of_slot = idx.ravel()[order]
+    rows = lay["perm_row"]
+    assert np.array_equal(lay["disp_token"][rows], t_of_slot)
+    ro = lay["rank_off"]
+    g_of_row = np.searchsorted(ro, rows, side="right") - 1
+    assert np.array_equal(g_of_row, place[e_of_slot])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_layout_small_random(orc, seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 10))
+    k = int(rng.integers(1, E + 1))
+    T = int(rng.integers(0, 40))
+    G = int(rng.integers(1, 6))
+    place = rng.integers(0, G, E).astype(np.int32)
+    idx = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+    check_layout(orc.layout(idx, E, place, G), idx, place, G, E)
+
+
+@pytest.mark.parametrize("wi,kind", [(0, "contiguous"), (1, "contiguous"), (1, "colocated"),
+                                     (2, "colocated"), (3, "contiguous"), (4, "colocated")])
+def test_layout_on_workloads(orc, wi, kind):
+    w = synth.workload(wi)
+    idx, _ = orc.route(synth.logits(w), w.k, w.n_groups, w.topk_groups)
+    place = synth.placement(w, kind)
+    if wi >= 3:   # python-set checks are slow at full size: check a token prefix
+        idx = idx[:3000]
+    check_layout(orc.layout(idx, w.E, place, w.G), idx, place, w.G, w.E)
+
+
+def test_layout_all_on_one_rank_and_one_rank_each(orc):
+    idx = np.array([[0, 1, 2], [2, 3, 0]], np.int32)
+    lay = orc.layout(idx, 4, np.zeros(4, np.int32), 1)
+    assert lay["R"] == 2 and list(lay["disp_token"]) == [0, 1]
+    lay = orc.layout(idx, 4, np.arange(4, dtype=np.int32), 4)
+    assert lay["R"] == 6
+
+
+def test_dispatch_rows_gather_identity(orc):
+    w = synth.workload(1)
+    idx, _ = orc.route(synth.logits(w), w.k)
+    lay = orc.layout(idx, w.E, synth.placement(w, "colocated"), w.G)
+    x = synth.activations(w)
+    xd = orc.dispatch_rows(x, lay["disp_token"])
+    assert xd.dtype == np.uint16 and np.array_equal(xd, x[lay["disp_token"]])
+
+
+# ------------------------------------------------------------------ FFN
+
+def np_swiglu(a, wg, wu, wd):
+    u = a @ wg.T
+    v = a @ wu.T
+    return (u * expit(u) * v) @ wd.T
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ffn_vs_matmul(orc, dtype):
+    w = synth.custom(T=37, d=48, E=3, k=2, F=80, G=2, dtype=dtype)
+    x = synth.activations(w)
+    wg, wu, wd = synth.weights(w)
+    rng = np.random.default_rng(1)
+    src = rng.integers(0, w.T, 50).astype(np.int32)
+    ex = rng.integers(0, w.E, 50).astype(np.int32)
+    y, h = orc.ffn_rows(x, src, ex, wg, wu, wd, want_h=True)
+    xf = synth.to_f64(x, dtype)
+    for i in range(50):
+        e = ex[i]
+        a = xf[src[i]]
+        G_, U_, D_ = (synth.to_f64(m[e], dtype) for m in (wg, wu, wd))
+        np.testing.assert_allclose(y[i], np_swiglu(a[None], G_, U_, D_)[0], rtol=1e-11, atol=1e-13)
+        u = G_ @ a
+        np.testing.assert_allclose(h[i], u * expit(u) * (U_ @ a), rtol=1e-11, atol=1e-13)
+
+
+def test_ffn_special_cases(orc):
+    w = synth.custom(T=20, d=32, E=2, k=1, F=24, G=1, dtype="bf16")
+    x = synth.activations(w)
+    wg, wu, wd = synth.weights(w)
+    src = np.arange(20, dtype=np.int32)
+    ex = (np.arange(20) % 2).astype(np.int32)
+    y = orc.ffn_rows(x, src, ex, wg, wu, wd)
+    # zero down-projection gives exactly zero
+    assert not orc.ffn_rows(x, src, ex, wg, wu, np.zeros_like(wd)).any()
+    # doubling the down-projection doubles y exactly (bf16 *2 is exact)
+    wd2 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(wd) * 2)
+    assert np.array_equal(orc.ffn_rows(x, src, ex, wg, wu, wd2), 2 * y)
+    # swapping gate and up changes the result (silu is not symmetric)
+    assert not np.allclose(orc.ffn_rows(x, src, ex, wu, wg, wd), y)
+
+
+# ------------------------------------------------------------------ combine / whole layer
+
+def test_combine_identity_experts_give_input(orc):
+    w = synth.workload(2)
+    w = synth.with_shape(w, T=512)
+    idx, g = orc.route(synth.logits(w), w.k)
+    lay = orc.layout(idx, w.E, synth.placement(w, "colocated"), w.G)
+    x = synth.to_f64(synth.activations(w), w.dtype)
+    y = x[lay["disp_token"][lay["perm_row"]]]             # identity experts
+    out = orc.combine(y, lay["slot_of"], g, w.T, w.k)
+    np.testing.assert_allclose(out, x, rtol=0, atol=1e-13 * np.abs(x).max())
+
+
+def test_combine_k1_is_permutation(orc):
+    rng = np.random.default_rng(3)
+    T, d = 33, 7
+    so = rng.permutation(T).astype(np.int32)
+    y = rng.standard_normal((T, d))
+    out = orc.combine(y, so, np.ones((T, 1)), T, 1)
+    assert np.array_equal(out, y[so])
+
+
+def test_layer_k_equals_E_is_dense_mixture(orc):
+    w = synth.custom(T=24, d=32, E=4, k=4, F=40, G=2, dtype="f32")
+    inp = synth.make(w)
+    r = orc.layer(inp["logits"], inp["x"], inp["place"], w.G, w.k,
+                  inp["w_gate"], inp["w_up"], inp["w_down"])
+    x = inp["x"].astype(np.float64)
+    p = softmax(inp["logits"].astype(np.float64), axis=1)   # softmax over all E
+    want = np.zeros((w.T, w.d))
+    for e in range(w.E):
+        ye = np_swiglu(x, inp["w_gate"][e].astype(np.float64), inp["w_up"][e].astype(np.float64),
+                       inp["w_down"][e].astype(np.float64))
+        want += p[:, e:e + 1] * ye
+    np.testing.assert_allclose(r["out"], want, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_vs_numpy_pipeline(orc, dtype):
+    w = synth.custom(T=150, d=64, E=8, k=3, F=96, G=4, dtype=dtype)
+    inp = synth.make(w)
+    r = orc.layer(inp["logits"], inp["x"], inp["place"], w.G, w.k,
+                  inp["w_gate"], inp["w_up"], inp["w_down"])
+    idx = lexsort_route(inp["logits"], w.k)
+    sel = np.take_along_axis(inp["logits"].astype(np.float64), idx, axis=1)
+    g = softmax(sel, axis=1)
+    x = synth.to_f64(inp["x"], dtype)
+    want = np.zeros((w.T, w.d))
+    for t in range(w.T):
+        for j in range(w.k):
+            e = idx[t, j]
+            want[t] += g[t, j] * np_swiglu(x[t:t + 1], *(synth.to_f64(m[e], dtype) for m in
+                                                        (inp["w_gate"], inp["w_up"], inp["w_down"])))[0]
+    np.testing.assert_allclose(r["out"], want, rtol=1e-10, atol=1e-12)
+
+
+def test_placement_invariance(orc):
+    """Placement changes neither the routing nor the layer's result (Zyphra page,
+    English abstract: the methods leave routing decisions and parameters alone)."""
+    w = synth.custom(T=200, d=32, E=8, k=3, F=48, G=4, dtype="bf16", clusters=4)
+    inp = synth.make(w)
+    res = []
+    for kind in ("contiguous", "colocated"):
+        pl = synth.placement(w, kind)
+        res.append(orc.layer(inp["logits"], inp["x"], pl, w.G, w.k,
+                             inp["w_gate"], inp["w_up"], inp["w_down"]))
+    a, b = res
+    for key in ("topk_idx", "gates", "coact", "expert_off", "slot_of", "y", "out"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["R"] != b["R"] or not np.array_equal(a["rank_mask"], b["rank_mask"])
+
+
+# ------------------------------------------------------------------ workload recipe
+
+def test_hot_bias_is_largest_grid_value_within_8x(orc):
+    w = synth.workload(3)
+    def ratio(h):
+        idx, _ = orc.route(synth.logits(w, hot_bias=h), w.k)
+        load = np.bincount(idx.ravel(), minlength=w.E)
+        return load.max() / load.mean()
+    h = synth.HOT_BIAS_T8192
+    assert ratio(h) <= 8.0
+    assert h == 8.0 or ratio(h + 0.125) > 8.0
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(0)
+    a = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    a[:4] = [1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 0.0]   # exact ties
+    ours = synth.f32_to_bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(synth.bf16_bits_to_f32(ours),
+                          torch.from_numpy(ours.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_generator_is_deterministic_and_subset_stable():
+    w = synth.custom(T=16, d=32, E=4, k=2, F=16, G=2, dtype="bf16")
+    a = synth.make(w)
+    b = synth.make(w)
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+    wg, wu, wd = synth.weights(w, experts=[2])
+    assert np.array_equal(wg[2], a["w_gate"][2]) and not wg[0].any()
