@@ -1,0 +1,292 @@
+// Dispatch layout: once-per-rank rows and the expert-grouped slot order.
+//
+// Zyphra correlated expert placement page, English abstract: experts sit on
+// GPUs according to a placement, and the dispatcher sends each token to each
+// GPU once. Here the G expert-parallel ranks are a map: the layout built is
+// exactly the send plan of such a dispatcher, and the dispatched rows are
+// the bytes it would send.
+//
+// Orders (fixed so that results are reproducible bit for bit):
+//  rows  : rank by rank, tokens ascending within a rank;
+//  slots : experts ascending, tokens ascending within an expert.
+//
+// gfx950 mapping. Tokens are cut into blocks of 256 (one per lane of a
+// 256-thread workgroup). A block sets one bit per (key, token) in LDS
+// bitmaps (key = expert or rank, 8 words of 32 tokens each) with atomicOr,
+// which commutes, so the bitmaps do not depend on timing. The stable rank of
+// a token among the block's tokens with the same key is a popcount of the
+// bits below it. Three launches:
+//   count   : per-block key counts and rank_mask;
+//   scan    : one workgroup turns the counts into per-block bases and the
+//             expert_off / rank_off prefixes (no host round trip: R stays on
+//             the device);
+//   scatter : disp_token, perm_row, slot_of and a per-token row list;
+// then a token-major copy reads each token row once and writes it to each
+// of its rows (16 bytes per lane).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBlockTok = 256;
+constexpr int kWords = kBlockTok / 32;
+
+struct BlockMasks {
+  uint32_t emask[kMaxE * kWords];
+  uint32_t rmask[kMaxG * kWords];
+  int32_t place[kMaxE];
+};
+
+// Builds the block's bitmaps; returns the token's rank mask (0 if t >= T).
+__device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk_idx, int T,
+                                int E, int k, const int32_t* __restrict__ place, int G) {
+  for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) sm.emask[i] = 0u;
+  for (int i = threadIdx.x; i < G * kWords; i += blockDim.x) sm.rmask[i] = 0u;
+  for (int i = threadIdx.x; i < E; i += blockDim.x) sm.place[i] = place[i];
+  __syncthreads();
+  const int t = blockIdx.x * kBlockTok + threadIdx.x;
+  const int w = threadIdx.x >> 5;
+  const uint32_t bit = 1u << (threadIdx.x & 31);
+  uint32_t m = 0u;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(size_t)t * k + j];
+      if (e < 0 || e >= E) continue;
+      const int g = sm.place[e];
+      if (g < 0 || g >= G) continue;
+      atomicOr(&sm.emask[e * kWords + w], bit);
+      m |= 1u << g;
+    }
+    for (uint32_t mm = m; mm; mm &= mm - 1) atomicOr(&sm.rmask[(__ffs(mm) - 1) * kWords + w], bit);
+  }
+  __syncthreads();
+  return m;
+}
+
+__global__ __launch_bounds__(kBlockTok) void layout_count_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
+    int G, uint32_t* __restrict__ rank_mask, int32_t* __restrict__ cnt) {
+  __shared__ BlockMasks sm;
+  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, G);
+  const int t = blockIdx.x * kBlockTok + threadIdx.x;
+  if (t < T) rank_mask[t] = m;
+  const int Q = E + G;
+  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
+    const uint32_t* mk = q < E ? &sm.emask[q * kWords] : &sm.rmask[(q - E) * kWords];
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) c += __popc(mk[w]);
+    cnt[(size_t)blockIdx.x * Q + q] = c;
+  }
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of n <= 256 values held in LDS by one wavefront (4 per lane).
+__device__ void wave_excl_scan_256(const int32_t* in, int32_t* out, int n, int32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = lane * 4 + i;
+    v[i] = q < n ? in[q] : 0;
+    s += v[i];
+  }
+  const int incl = wave_incl_scan(s);
+  int run = incl - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = lane * 4 + i;
+    if (q < n) out[q] = run;
+    run += v[i];
+  }
+  if (lane == kWave - 1) *total = incl;
+}
+
+__global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__ cnt, int nblk,
+                                                           int E, int G,
+                                                           int32_t* __restrict__ expert_off,
+                                                           int32_t* __restrict__ rank_off) {
+  __shared__ int32_t tot[kMaxE + kMaxG];
+  __shared__ int32_t off[kMaxE + kMaxG];
+  const int Q = E + G;
+  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
+    int s = 0;
+    for (int b = 0; b < nblk; ++b) s += cnt[(size_t)b * Q + q];
+    tot[q] = s;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x / kWave;
+  if (wave == 0) wave_excl_scan_256(tot, off, E, &expert_off[E]);
+  if (wave == 1) wave_excl_scan_256(tot + E, off + E, G, &rank_off[G]);
+  __syncthreads();
+  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
+    int run = off[q];
+    if (q < E) expert_off[q] = run;
+    else rank_off[q - E] = run;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = cnt[(size_t)b * Q + q];
+      cnt[(size_t)b * Q + q] = run;
+      run += c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlockTok) void layout_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
+    int G, const int32_t* __restrict__ base_in, int32_t* __restrict__ disp_token,
+    int32_t* __restrict__ perm_row, int32_t* __restrict__ slot_of,
+    int32_t* __restrict__ tok_rows) {
+  __shared__ BlockMasks sm;
+  __shared__ int32_t epre[kMaxE * kWords];
+  __shared__ int32_t rpre[kMaxG * kWords];
+  __shared__ int32_t base[kMaxE + kMaxG];
+  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, G);
+  const int Q = E + G;
+  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
+    const uint32_t* mk = q < E ? &sm.emask[q * kWords] : &sm.rmask[(q - E) * kWords];
+    int32_t* pre = q < E ? &epre[q * kWords] : &rpre[(q - E) * kWords];
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) {
+      pre[w] = run;
+      run += __popc(mk[w]);
+    }
+    base[q] = base_in[(size_t)blockIdx.x * Q + q];
+  }
+  __syncthreads();
+  const int t = blockIdx.x * kBlockTok + threadIdx.x;
+  if (t >= T) return;
+  const int w = threadIdx.x >> 5;
+  const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
+  int n = 0;
+  for (uint32_t mm = m; mm; mm &= mm - 1) {
+    const int g = __ffs(mm) - 1;
+    const int row = base[E + g] + rpre[g * kWords + w] + __popc(sm.rmask[g * kWords + w] & below);
+    disp_token[row] = t;
+    tok_rows[(size_t)t * k + n++] = row;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(size_t)t * k + j];
+    if (e < 0 || e >= E) continue;
+    const int g = sm.place[e];
+    if (g < 0 || g >= G) continue;
+    const int row = base[E + g] + rpre[g * kWords + w] + __popc(sm.rmask[g * kWords + w] & below);
+    const int s = base[e] + epre[e * kWords + w] + __popc(sm.emask[e * kWords + w] & below);
+    perm_row[s] = row;
+    slot_of[(size_t)t * k + j] = s;
+  }
+}
+
+// Token-major row copy: one wavefront per token reads its row once and
+// writes it to each of the token's rows.
+__global__ __launch_bounds__(256) void dispatch_rows_kernel(const uint4* __restrict__ x, int T,
+                                                            int row_vecs, int k,
+                                                            const uint32_t* __restrict__ rank_mask,
+                                                            const int32_t* __restrict__ tok_rows,
+                                                            uint4* __restrict__ x_disp) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int n = __popc(rank_mask[t]);
+  int rows[kMaxK];
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i) rows[i] = i < n ? tok_rows[(size_t)t * k + i] : 0;
+  const uint4* src = x + (size_t)t * row_vecs;
+  constexpr int U = 4;
+  for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < row_vecs) v[u] = src[c];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) {
+      if (i < n) {
+        uint4* dst = x_disp + (size_t)rows[i] * row_vecs;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * kWave + lane;
+          if (c < row_vecs) dst[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Workspace {
+  size_t cnt_bytes, rows_bytes, total;
+};
+inline Workspace workspace_layout(int32_t T, int32_t E, int32_t k, int32_t G) {
+  Workspace w;
+  const size_t nblk = (size_t)ceil_div(T, kBlockTok);
+  w.cnt_bytes = align_up(nblk * (size_t)(E + G) * sizeof(int32_t));
+  w.rows_bytes = align_up((size_t)T * k * sizeof(int32_t));
+  w.total = w.cnt_bytes + w.rows_bytes;
+  if (w.total == 0) w.total = kAlign;
+  return w;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+MOE_EXPORT size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t G) {
+  if (T < 0 || E < 1 || k < 1 || G < 1) return 0;
+  return workspace_layout(T, E, k, G).total;
+}
+
+MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                          const int32_t* place, int32_t G, const void* x, int32_t d,
+                                          moe_dtype dt, uint32_t* rank_mask, int32_t* rank_off,
+                                          int32_t* disp_token, int32_t* expert_off,
+                                          int32_t* perm_row, int32_t* slot_of, void* x_disp,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || G < 1) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK || G > kMaxG || (int64_t)T * k >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (!place || !rank_off || !expert_off) return MOE_ERR_ARG;
+  if (T > 0 && (!topk_idx || !rank_mask || !disp_token || !perm_row || !slot_of))
+    return MOE_ERR_ARG;
+  if (x) {
+    if (!valid_dtype(dt) || d < 1 || (T > 0 && !x_disp)) return MOE_ERR_ARG;
+    if (((size_t)d * dtype_bytes(dt)) % 16 != 0 || (uintptr_t)x % 16 || (uintptr_t)x_disp % 16)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  const Workspace ws = workspace_layout(T, E, k, G);
+  if (!workspace || workspace_bytes < ws.total) return MOE_ERR_WORKSPACE;
+  int32_t* cnt = static_cast<int32_t*>(workspace);
+  int32_t* tok_rows = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws.cnt_bytes);
+  const int nblk = (int)ceil_div(T, kBlockTok);
+
+  if (nblk > 0)
+    hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(kBlockTok), 0, stream, topk_idx, T,
+                       E, k, place, G, rank_mask, cnt);
+  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, nblk, E, G,
+                     expert_off, rank_off);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(kBlockTok), 0, stream, topk_idx,
+                       T, E, k, place, G, cnt, disp_token, perm_row, slot_of, tok_rows);
+    if (x) {
+      const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);
+      hipLaunchKernelGGL(dispatch_rows_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+                         stream, static_cast<const uint4*>(x), T, row_vecs, k, rank_mask,
+                         tok_rows, static_cast<uint4*>(x_disp));
+    }
+  }
+  return launch_status();
+}

@@ -1,0 +1,248 @@
+"""Python binding of libmoe (include/moe.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls, takes torch device
+tensors (torch is used for device memory and streams only), allocates any
+output that is not passed in, and raises ``MoeError`` on a non-OK status.
+Every step of the hot path runs in the HIP kernels of libmoe.so; there is no
+fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+
+
+def lib():
+    """Load libmoe.so (built in-tree); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        p, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        sig = {
+            "moe_abi_version": (C.c_int, []),
+            "moe_status_str": (C.c_char_p, [C.c_int]),
+            "moe_route": (C.c_int, [p, i32, i32, i32, i32, i32, p, p, p]),
+            "moe_coact_hist": (C.c_int, [p, i32, i32, i32, p, p]),
+            "moe_dispatch_workspace_bytes": (sz, [i32, i32, i32, i32]),
+            "moe_dispatch_layout": (C.c_int, [p, i32, i32, i32, p, i32, p, i32, C.c_int,
+                                              p, p, p, p, p, p, p, p, sz, p]),
+            "moe_expert_gate_up": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p, C.c_int,
+                                             p, p]),
+            "moe_expert_down": (C.c_int, [p, p, i32, i32, i32, i32, i32, p, C.c_int, p, p]),
+            "moe_grouped_ffn": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p, p, C.c_int,
+                                          p, p, p]),
+            "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/moe.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", txt)))
+
+
+def status_str(s: int) -> str:
+    return lib().moe_status_str(int(s)).decode()
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activations and weights must be float32 or bfloat16, got {t.dtype}")
+
+
+# ---------------------------------------------------------------- entry points
+
+def moe_route(logits, k, n_groups=1, topk_groups=1, topk_idx=None, gates=None, stream=None):
+    T, E = logits.shape
+    dev = logits.device
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev) if gates is None else gates
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    _check("moe_route", lib().moe_route(_ptr(logits), T, E, k, n_groups, topk_groups,
+                                        _ptr(topk_idx), _ptr(gates), _stream(stream)))
+    return topk_idx, gates
+
+
+def moe_coact_hist(topk_idx, E, coact=None, stream=None):
+    T, k = topk_idx.shape
+    coact = torch.zeros((E, E), dtype=torch.int32, device=topk_idx.device) if coact is None else coact
+    _check("moe_coact_hist", lib().moe_coact_hist(_ptr(topk_idx), T, E, k, _ptr(coact),
+                                                  _stream(stream)))
+    return coact
+
+
+def moe_dispatch_workspace_bytes(T, E, k, G):
+    return int(lib().moe_dispatch_workspace_bytes(T, E, k, G))
+
+
+def alloc_layout(T, E, k, G, device, d=None, dtype=None):
+    """Output buffers of moe_dispatch_layout, sized for the T*k upper bound."""
+    i32 = dict(dtype=torch.int32, device=device)
+    out = dict(rank_mask=torch.empty(T, dtype=torch.int32, device=device),
+               rank_off=torch.empty(G + 1, **i32), disp_token=torch.empty(T * k, **i32),
+               expert_off=torch.empty(E + 1, **i32), perm_row=torch.empty(T * k, **i32),
+               slot_of=torch.empty(T * k, **i32),
+               workspace=torch.empty(max(1, moe_dispatch_workspace_bytes(T, E, k, G)),
+                                     dtype=torch.uint8, device=device))
+    if d is not None:
+        out["x_disp"] = torch.empty((T * k, d), dtype=dtype, device=device)
+    return out
+
+
+def moe_dispatch_layout(topk_idx, E, place, G, x=None, out=None, stream=None):
+    """Returns the dict of outputs (rank_mask holds uint32 bits in an int32 tensor)."""
+    T, k = topk_idx.shape
+    d = x.shape[1] if x is not None else None
+    if out is None:
+        out = alloc_layout(T, E, k, G, topk_idx.device, d, x.dtype if x is not None else None)
+    dt = dtype_code(x) if x is not None else MOE_F32
+    ws = out["workspace"]
+    _check("moe_dispatch_layout", lib().moe_dispatch_layout(
+        _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(x), d or 0, dt,
+        _ptr(out["rank_mask"]), _ptr(out["rank_off"]), _ptr(out["disp_token"]),
+        _ptr(out["expert_off"]), _ptr(out["perm_row"]), _ptr(out["slot_of"]),
+        _ptr(out.get("x_disp")) if x is not None else None, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def moe_expert_gate_up(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=None, stream=None):
+    E, F, d = w_gate.shape
+    h = torch.empty((T * k, F), dtype=x_disp.dtype, device=x_disp.device) if h is None else h
+    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+        _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
+        dtype_code(x_disp), _ptr(h), _stream(stream)))
+    return h
+
+
+def moe_expert_down(h, expert_off, T, k, w_down, y=None, stream=None):
+    E, d, F = w_down.shape
+    y = torch.empty((T * k, d), dtype=h.dtype, device=h.device) if y is None else y
+    _check("moe_expert_down", lib().moe_expert_down(
+        _ptr(h), _ptr(expert_off), T, E, k, d, F, _ptr(w_down), dtype_code(h), _ptr(y),
+        _stream(stream)))
+    return y
+
+
+def moe_grouped_ffn(x_disp, perm_row, expert_off, T, k, w_gate, w_up, w_down, h=None, y=None,
+                    stream=None):
+    E, F, d = w_gate.shape
+    dev, dt = x_disp.device, x_disp.dtype
+    h = torch.empty((T * k, F), dtype=dt, device=dev) if h is None else h
+    y = torch.empty((T * k, d), dtype=dt, device=dev) if y is None else y
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(
+        _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), dtype_code(x_disp), _ptr(h), _ptr(y), _stream(stream)))
+    return h, y
+
+
+def moe_combine(y, slot_of, gates, T, k, out=None, stream=None):
+    d = y.shape[1]
+    out = torch.empty((T, d), dtype=y.dtype, device=y.device) if out is None else out
+    _check("moe_combine", lib().moe_combine(_ptr(y), _ptr(slot_of), _ptr(gates), T, k, d,
+                                            dtype_code(y), _ptr(out), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- whole layer
+
+class Layer:
+    """Preallocated buffers for repeated passes of the hot path on one shape."""
+
+    def __init__(self, T, d, E, k, F, G, dtype, device, n_groups=1, topk_groups=1):
+        self.T, self.d, self.E, self.k, self.F, self.G = T, d, E, k, F, G
+        self.n_groups, self.topk_groups = n_groups, topk_groups
+        dev = torch.device(device)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.coact = torch.zeros((E, E), dtype=torch.int32, device=dev)
+        self.lay = alloc_layout(T, E, k, G, dev, d, dtype)
+        self.h = torch.empty((T * k, F), dtype=dtype, device=dev)
+        self.y = torch.empty((T * k, d), dtype=dtype, device=dev)
+        self.out = torch.empty((T, d), dtype=dtype, device=dev)
+
+    def route(self, logits, stream=None):
+        moe_route(logits, self.k, self.n_groups, self.topk_groups, self.topk_idx, self.gates,
+                  stream)
+
+    def coact_hist(self, stream=None):
+        moe_coact_hist(self.topk_idx, self.E, self.coact, stream)
+
+    def dispatch(self, x, place, stream=None):
+        moe_dispatch_layout(self.topk_idx, self.E, place, self.G, x, self.lay, stream)
+
+    def gate_up(self, w_gate, w_up, stream=None):
+        moe_expert_gate_up(self.lay["x_disp"], self.lay["perm_row"], self.lay["expert_off"],
+                           self.T, self.k, w_gate, w_up, self.h, stream)
+
+    def down(self, w_down, stream=None):
+        moe_expert_down(self.h, self.lay["expert_off"], self.T, self.k, w_down, self.y, stream)
+
+    def combine(self, stream=None):
+        moe_combine(self.y, self.lay["slot_of"], self.gates, self.T, self.k, self.out, stream)
+
+    def forward(self, logits, x, place, w_gate, w_up, w_down, stream=None):
+        """One pass of the whole hot path; the co-activation counts accumulate."""
+        self.route(logits, stream)
+        self.coact_hist(stream)
+        self.dispatch(x, place, stream)
+        self.gate_up(w_gate, w_up, stream)
+        self.down(w_down, stream)
+        self.combine(stream)
+        return self.out

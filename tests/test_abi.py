@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+function, and rejects bad arguments before enqueuing any GPU work (none of
+these calls touches a device, so they run without a GPU)."""
+import ctypes as C
+
+import pytest
+
+from routing_dispatch_expert_top_amd import ops
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ops.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = ops.header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    assert ops.status_str(0) == "ok"
+    assert "workspace" in ops.status_str(3)
+    assert ops.status_str(99) == "unknown status"
+
+
+def test_workspace_bytes_host_only(L):
+    a = ops.moe_dispatch_workspace_bytes(8192, 128, 8, 16)
+    b = ops.moe_dispatch_workspace_bytes(16384, 128, 8, 16)
+    assert 0 < a < b and a % 256 == 0
+    assert ops.moe_dispatch_workspace_bytes(0, 8, 2, 4) > 0
+    assert ops.moe_dispatch_workspace_bytes(-1, 8, 2, 4) == 0
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("args,want", [
+    ((NULL, 4, 8, 9, 1, 1, NULL, NULL, NULL), ops.MOE_ERR_ARG),          # k > E
+    ((NULL, 4, 8, 0, 1, 1, NULL, NULL, NULL), ops.MOE_ERR_ARG),          # k < 1
+    ((NULL, -1, 8, 2, 1, 1, NULL, NULL, NULL), ops.MOE_ERR_ARG),         # T < 0
+    ((NULL, 4, 8, 2, 3, 1, NULL, NULL, NULL), ops.MOE_ERR_ARG),          # groups do not divide E
+    ((NULL, 4, 8, 2, 4, 5, NULL, NULL, NULL), ops.MOE_ERR_ARG),          # topk_groups > n_groups
+    ((NULL, 4, 8, 5, 4, 2, NULL, NULL, NULL), ops.MOE_ERR_ARG),          # < k eligible experts
+    ((NULL, 4, 512, 2, 1, 1, NULL, NULL, NULL), ops.MOE_ERR_UNSUPPORTED),  # E > 256
+    ((NULL, 4, 64, 17, 1, 1, NULL, NULL, NULL), ops.MOE_ERR_UNSUPPORTED),  # k > 16
+    ((NULL, 4, 8, 2, 1, 1, NULL, NULL, NULL), ops.MOE_ERR_ARG),          # null pointers
+    ((NULL, 0, 8, 2, 1, 1, NULL, NULL, NULL), ops.MOE_OK),               # empty: nothing to do
+])
+def test_route_argument_errors(L, args, want):
+    assert L.moe_route(*args) == want
+
+
+def test_coact_argument_errors(L):
+    assert L.moe_coact_hist(NULL, 4, 8, 9, NULL, NULL) == ops.MOE_ERR_ARG
+    assert L.moe_coact_hist(NULL, 4, 300, 2, NULL, NULL) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_coact_hist(NULL, 4, 8, 2, NULL, NULL) == ops.MOE_ERR_ARG
+    assert L.moe_coact_hist(NULL, 0, 8, 2, NULL, NULL) == ops.MOE_OK
+    assert L.moe_coact_hist(NULL, 4, 8, 1, NULL, NULL) == ops.MOE_OK   # k=1: no pairs
+
+
+def _layout(L, T=4, E=8, k=2, G=4, place=1, ws=None, wsb=0, x=None, d=0, dt=1, ptr=1):
+    p = ptr or None
+    return L.moe_dispatch_layout(p, T, E, k, place or None, G, x, d, dt, p, p, p, p, p, p, p,
+                                 ws, wsb, None)
+
+
+def test_layout_argument_errors(L):
+    assert _layout(L, G=0) == ops.MOE_ERR_ARG
+    assert _layout(L, G=33) == ops.MOE_ERR_UNSUPPORTED
+    assert _layout(L, k=9) == ops.MOE_ERR_ARG
+    assert _layout(L, place=0) == ops.MOE_ERR_ARG
+    assert _layout(L, ptr=0) == ops.MOE_ERR_ARG
+    assert _layout(L) == ops.MOE_ERR_WORKSPACE                       # no workspace
+    need = ops.moe_dispatch_workspace_bytes(4, 8, 2, 4)
+    assert _layout(L, ws=16, wsb=need - 1) == ops.MOE_ERR_WORKSPACE  # too small
+    assert _layout(L, ws=16, wsb=need, x=16, d=3) == ops.MOE_ERR_UNSUPPORTED  # row not 16B
+    assert _layout(L, ws=16, wsb=need, x=16, d=64, dt=7) == ops.MOE_ERR_ARG   # bad dtype
+
+
+def test_ffn_and_combine_argument_errors(L):
+    p = 16
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 100, 64, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 96, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(None, p, p, 4, 8, 2, 64, 64, p, p, 1, p, None) == ops.MOE_ERR_ARG
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 64, p, p, 5, p, None) == ops.MOE_ERR_ARG
+    assert L.moe_expert_down(p, p, 4, 8, 9, 64, 64, p, 1, p, None) == ops.MOE_ERR_ARG
+    assert L.moe_expert_down(None, p, 4, 8, 2, 64, 64, p, 1, p, None) == ops.MOE_ERR_ARG
+    assert L.moe_grouped_ffn(p, p, p, 0, 8, 2, 64, 64, p, p, p, 1, p, p, None) == ops.MOE_OK
+    assert L.moe_combine(p, p, p, 4, 0, 64, 1, p, None) == ops.MOE_ERR_ARG
+    assert L.moe_combine(p, p, p, 4, 2, 4, 1, p, None) == ops.MOE_ERR_UNSUPPORTED  # 8-byte rows
+    assert L.moe_combine(None, p, p, 4, 2, 64, 1, p, None) == ops.MOE_ERR_ARG
+    assert L.moe_combine(p, p, p, 0, 2, 64, 1, p, None) == ops.MOE_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ops.moe_route(torch.zeros(4, 8), 2)
