@@ -56,6 +56,8 @@ def _bind(L):
     L.orc_dispatch_rows.argtypes = [p, i, i, i, p, i, p]
     L.orc_ffn_rows.argtypes = [p, i, i, i, i, p, p, i, p, p, p, p, p]
     L.orc_combine.argtypes = [p, i, p, p, i, i, i, p]
+    L.orc_threads.argtypes = []
+    L.orc_threads.restype = C.c_int
     for f in (L.orc_route, L.orc_coact, L.orc_layout, L.orc_dispatch_rows,
               L.orc_ffn_rows, L.orc_combine):
         f.restype = C.c_int
@@ -100,6 +102,11 @@ def _dt(a: np.ndarray) -> int:
     if a.dtype == np.uint16:
         return BF16
     raise TypeError(f"activations/weights must be float32 or bf16 bits (uint16), got {a.dtype}")
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())
 
 
 # ---------------------------------------------------------------- step wrappers

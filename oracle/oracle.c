@@ -30,11 +30,24 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_F32 0
 #define ORC_BF16 1
 
 int orc_version(void) { return 1; }
+
+/* Threads the parallel loops use. */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Exact widening of one stored element to double. */
 static double orc_elem(const void* base, size_t i, int dt)

@@ -200,10 +200,10 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const uint4* __restr
   int rows[kMaxK];
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i) rows[i] = i < n ? tok_rows[(size_t)t * k + i] : 0;
-  const uint4* src = x + (size_t)t * row_vecs;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * row_vecs;
   constexpr int U = 4;
   for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave + lane;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const uint4* __restr
 #pragma unroll
     for (int i = 0; i < kMaxK; ++i) {
       if (i < n) {
-        uint4* dst = x_disp + (size_t)rows[i] * row_vecs;
+        u32x4* dst = reinterpret_cast<u32x4*>(x_disp) + (size_t)rows[i] * row_vecs;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = c0 + u * kWave + lane;

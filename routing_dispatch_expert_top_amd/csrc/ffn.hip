@@ -118,8 +118,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C) {
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int CH = Cfg::kChunks;
-  __shared__ uint4 As[2][BM * CH];
-  __shared__ uint4 Bs[2][BN * CH];
+  __shared__ u32x4 As[2][BM * CH];
+  __shared__ u32x4 Bs[2][BN * CH];
   __shared__ Sched sc;
 
   build_schedule(sc, expert_off, E, BM);
@@ -134,8 +134,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 
   const int tid = threadIdx.x;
   // global source rows of this thread's A and B chunks (fixed over K)
-  const uint4* aptr[Cfg::kALoads];
-  const uint4* bptr[Cfg::kBLoads];
+  const u32x4* aptr[Cfg::kALoads];
+  const u32x4* bptr[Cfg::kBLoads];
   const size_t kvec = (size_t)K / 8;  // 16-byte chunks per K row
 #pragma unroll
   for (int i = 0; i < Cfg::kALoads; ++i) {
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const int r = q / CH, c = q % CH;
     const int s = min(m0 + r, seg1 - 1);
     const int src = perm_row ? perm_row[s] : s;
-    aptr[i] = reinterpret_cast<const uint4*>(A) + (size_t)src * kvec + c;
+    aptr[i] = reinterpret_cast<const u32x4*>(A) + (size_t)src * kvec + c;
   }
 #pragma unroll
   for (int i = 0; i < Cfg::kBLoads; ++i) {
@@ -159,46 +159,44 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       n = c0 + r;
     }
     n = min(n, N0 - 1);
-    bptr[i] = reinterpret_cast<const uint4*>(base) + ((size_t)e * N0 + n) * kvec + c;
+    bptr[i] = reinterpret_cast<const u32x4*>(base) + ((size_t)e * N0 + n) * kvec + c;
   }
 
-  uint4 ra[Cfg::kALoads], rb[Cfg::kBLoads];
-  auto load_regs = [&](int kt) {
+  // LDS slot (16-byte units) of each staged chunk: row r, chunk c -> r*8 + (c ^ (r & 7))
+  int a_lds[Cfg::kALoads], b_lds[Cfg::kBLoads];
 #pragma unroll
-    for (int i = 0; i < Cfg::kALoads; ++i) ra[i] = aptr[i][(size_t)kt * CH];
+  for (int i = 0; i < Cfg::kALoads; ++i) {
+    const int q = tid + i * Cfg::kThreads;
+    const int r = q / CH, c = q % CH;
+    a_lds[i] = r * CH + (c ^ (r & 7));
+  }
 #pragma unroll
-    for (int i = 0; i < Cfg::kBLoads; ++i) rb[i] = bptr[i][(size_t)kt * CH];
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < Cfg::kALoads; ++i) {
-      const int q = tid + i * Cfg::kThreads;
-      const int r = q / CH, c = q % CH;
-      As[buf][r * CH + (c ^ (r & 7))] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::kBLoads; ++i) {
-      const int q = tid + i * Cfg::kThreads;
-      const int r = q / CH, c = q % CH;
-      Bs[buf][r * CH + (c ^ (r & 7))] = rb[i];
-    }
-  };
+  for (int i = 0; i < Cfg::kBLoads; ++i) {
+    const int q = tid + i * Cfg::kThreads;
+    const int r = q / CH, c = q % CH;
+    b_lds[i] = r * CH + (c ^ (r & 7));
+  }
 
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * Cfg::kWaveRows;
-  // B rows of the wave's N tiles: gate/up pairs for SWIGLU
-  int brow[Cfg::TN];
+  const int li = lane & 31, lk = lane >> 5;
+  // LDS slots of the MFMA fragments for k-step 0 (k-step ks adds 2*ks to the
+  // chunk, i.e. XORs 2*ks into the swizzled chunk index)
+  int fa_row[Cfg::TM], fb_row[Cfg::TN];
+#pragma unroll
+  for (int tm = 0; tm < Cfg::TM; ++tm) fa_row[tm] = arow0 + tm * 32 + li;
 #pragma unroll
   for (int tn = 0; tn < Cfg::TN; ++tn) {
+    int br;
     if (SWIGLU) {
       constexpr int half = Cfg::TN / 2;
-      const int fw0 = wn * (Cfg::kWaveCols / 2);
-      brow[tn] = (tn < half ? 0 : BN / 2) + fw0 + (tn % half) * 32;
+      br = (tn < half ? 0 : BN / 2) + wn * (Cfg::kWaveCols / 2) + (tn % half) * 32;
     } else {
-      brow[tn] = wn * Cfg::kWaveCols + tn * 32;
+      br = wn * Cfg::kWaveCols + tn * 32;
     }
+    fb_row[tn] = br + li;
   }
 
   f32x16 acc[Cfg::TM][Cfg::TN];
@@ -210,34 +208,53 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = K / Cfg::kBK;
-  load_regs(0);
-  store_lds(0);
+  u32x4 ra[Cfg::kALoads], rb[Cfg::kBLoads];
+#pragma unroll
+  for (int i = 0; i < Cfg::kALoads; ++i) ra[i] = aptr[i][0];
+#pragma unroll
+  for (int i = 0; i < Cfg::kBLoads; ++i) rb[i] = bptr[i][0];
+#pragma unroll
+  for (int i = 0; i < Cfg::kALoads; ++i) As[0][a_lds[i]] = ra[i];
+#pragma unroll
+  for (int i = 0; i < Cfg::kBLoads; ++i) Bs[0][b_lds[i]] = rb[i];
   __syncthreads();
-  const int li = lane & 31, lk = lane >> 5;
+
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load_regs(kt + 1);
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const size_t off = (size_t)(kt + 1) * CH;
+#pragma unroll
+      for (int i = 0; i < Cfg::kALoads; ++i) ra[i] = aptr[i][off];
+#pragma unroll
+      for (int i = 0; i < Cfg::kBLoads; ++i) rb[i] = bptr[i][off];
+    }
+    const u32x4* as = As[cur];
+    const u32x4* bs = Bs[cur];
 #pragma unroll
     for (int ks = 0; ks < Cfg::kBK / 16; ++ks) {
       const int ch = ks * 2 + lk;
       bf16x8 fa[Cfg::TM], fb[Cfg::TN];
 #pragma unroll
-      for (int tm = 0; tm < Cfg::TM; ++tm) {
-        const int r = arow0 + tm * 32 + li;
-        fa[tm] = __builtin_bit_cast(bf16x8, As[cur][r * CH + (ch ^ (r & 7))]);
-      }
+      for (int tm = 0; tm < Cfg::TM; ++tm)
+        fa[tm] = __builtin_bit_cast(bf16x8, as[fa_row[tm] * CH + (ch ^ (fa_row[tm] & 7))]);
 #pragma unroll
-      for (int tn = 0; tn < Cfg::TN; ++tn) {
-        const int r = brow[tn] + li;
-        fb[tn] = __builtin_bit_cast(bf16x8, Bs[cur][r * CH + (ch ^ (r & 7))]);
-      }
+      for (int tn = 0; tn < Cfg::TN; ++tn)
+        fb[tn] = __builtin_bit_cast(bf16x8, bs[fb_row[tn] * CH + (ch ^ (fb_row[tn] & 7))]);
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < Cfg::TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
     }
-    if (kt + 1 < KT) store_lds(cur ^ 1);
+    if (more) {
+      u32x4* asn = As[cur ^ 1];
+      u32x4* bsn = Bs[cur ^ 1];
+#pragma unroll
+      for (int i = 0; i < Cfg::kALoads; ++i) asn[a_lds[i]] = ra[i];
+#pragma unroll
+      for (int i = 0; i < Cfg::kBLoads; ++i) bsn[b_lds[i]] = rb[i];
+    }
     __syncthreads();
   }
 

@@ -20,6 +20,7 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, a native vector
 
 // fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
