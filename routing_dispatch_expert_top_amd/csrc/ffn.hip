@@ -12,10 +12,10 @@
 // bf16 path (gfx950): v_mfma_f32_32x32x16_bf16, fp32 accumulation. A
 // workgroup computes a BM x BN tile (BN counts B rows: for gate/up, half
 // gate rows and half up rows of the same F columns, so the epilogue has u
-// and v of an element in the same lane). The K loop stages 64-wide K slices
-// of A and B through double-buffered LDS (16-byte chunks, XOR-swizzled by
-// row so the MFMA fragment reads spread over the banks), prefetching the
-// next slice into registers while the MFMAs run on the current one.
+// and v of an element in the same lane). The K loop streams K slices of A
+// and B into a ring of LDS stages with direct-to-LDS loads (16-byte chunks,
+// XOR-swizzled so the MFMA fragment reads are free of bank conflicts) while
+// the MFMAs consume an earlier slice.
 // The tile list is derived on the device from expert_off (each workgroup
 // scans it in LDS), so no host round trip is needed; blocks are remapped so
 // that consecutive tiles of one (expert, N-tile) land on the same XCD and
@@ -97,58 +97,130 @@ __device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f +
 template <int BM, int BN, int WM, int WN, bool SWIGLU>
 struct TileCfg {
   static constexpr int kThreads = WM * WN * kWave;
-  static constexpr int kBK = 64;                  // K per LDS stage
-  static constexpr int kChunks = kBK / 8;         // 16-byte chunks per row
   static constexpr int kWaveRows = BM / WM;
   static constexpr int kWaveCols = BN / WN;       // B rows per wave
   static constexpr int TM = kWaveRows / 32;
   static constexpr int TN = kWaveCols / 32;
   static constexpr int kOutCols = SWIGLU ? BN / 2 : BN;
-  static constexpr int kALoads = BM * kChunks / kThreads;
-  static constexpr int kBLoads = BN * kChunks / kThreads;
   static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "tile shape");
   static_assert(!SWIGLU || TN % 2 == 0, "gate/up pairs");
-  static_assert((BM * kChunks) % kThreads == 0 && (BN * kChunks) % kThreads == 0, "loads");
 };
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU>
+// ---------------------------------------------------------------- bf16 MFMA kernel
+//
+// K slices travel HBM/L2 -> LDS with
+// gfx950's 16-byte direct-to-LDS loads (global_load_lds_dwordx4: each lane's
+// 16 bytes land at wave base + 16 * lane), so no registers stage them and up
+// to NS-1 slices are in flight while the MFMAs consume another. One DMA
+// instruction fills 8 LDS rows of 128 bytes; a lane picks the global chunk
+// whose swizzled slot is its own, so the LDS image is the XOR-swizzled one
+// the fragment reads expect. Waits are explicit (vmcnt = DMA instructions
+// still allowed in flight) and the workgroup barrier carries no memory fence,
+// so the compiler does not drain every outstanding load at each K step.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte direct-to-LDS load per lane into the wave's 1 KiB LDS window at
+// lds_base. Issued as inline asm so the compiler does not add its own
+// "wait for every LDS DMA" before later LDS reads; completion is tracked by
+// the explicit vmcnt waits of the K loop (VMEM ops count in issue order, so
+// the compiler's own waits for earlier loads stay correct).
+__device__ __forceinline__ void dma16(const u32x4* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  // M0 carries the LDS base; it is restored so the compiler's view of M0 holds
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// LDS slot of chunk c of row r when a K slice has CH 16-byte chunks per row
+// (CH = 8: 128-byte rows, CH = 4: 64-byte rows). 256 bytes of LDS cover all
+// banks; the fragment reads take 16 consecutive rows at one logical chunk,
+// and XOR-ing the chunk with the row's index among the rows sharing a bank
+// phase gives those 16 rows 16 distinct 16-byte bank groups.
+template <int CH>
+__device__ __forceinline__ int swz_ch(int r, int c) {
+  constexpr int kRowsPer256 = 16 / CH;
+  return r * CH + (c ^ ((r / kRowsPer256) & (CH - 1)));
+}
+
+// DMA of one K slice: instruction i of a wave fills rows [RPI*(wave+NW*i), +RPI)
+template <int N, int NW, int RPI, int CH>
+__device__ __forceinline__ void dma_slice(const u32x4* const (&src)[N], u32x4* stage, int wave,
+                                          size_t koff) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    dma16(src[i] + koff,
+          __builtin_amdgcn_readfirstlane(lds_addr(stage + (RPI * (wave + NW * i)) * CH)));
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool SWIGLU>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C) {
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
-  constexpr int CH = Cfg::kChunks;
-  __shared__ u32x4 As[2][BM * CH];
-  __shared__ u32x4 Bs[2][BN * CH];
+  constexpr int NW = WM * WN;
+  constexpr int CH = BK / 8;            // 16-byte chunks per row of a K slice
+  constexpr int RPI = 512 / BK;         // rows filled by one 1 KiB DMA instruction
+  constexpr int A_INS = BM / RPI / NW;  // DMA instructions per wave per slice
+  constexpr int B_INS = BN / RPI / NW;
+  constexpr int LPS = A_INS + B_INS;
+  static_assert(BK == 32 || BK == 64, "K slice");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA row split");
+  static_assert(NS >= 2 && (NS - 2) * LPS <= 63, "pipeline depth");
+  __shared__ u32x4 As[NS][BM * CH];
+  __shared__ u32x4 Bs[NS][BN * CH];
   __shared__ Sched sc;
 
   build_schedule(sc, expert_off, E, BM);
   const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
-  const int tile = xcd_logical_tile(sc.mt_off[E] * NT);
+  const int total = sc.mt_off[E] * NT;
+  const int tile = xcd_logical_tile(total);
   if (tile < 0) return;
   int e, nt, mt;
   decode_tile(sc, E, NT, tile, e, nt, mt);
   const int seg0 = expert_off[e], seg1 = expert_off[e + 1];
   const int m0 = seg0 + mt * BM;
-  const int c0 = nt * Cfg::kOutCols;  // first output column of the tile
+  const int c0 = nt * Cfg::kOutCols;
 
   const int tid = threadIdx.x;
-  // global source rows of this thread's A and B chunks (fixed over K)
-  const u32x4* aptr[Cfg::kALoads];
-  const u32x4* bptr[Cfg::kBLoads];
-  const size_t kvec = (size_t)K / 8;  // 16-byte chunks per K row
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const size_t kvec = (size_t)K / 8;
+  const u32x4* A4 = reinterpret_cast<const u32x4*>(A);
+  const u32x4* asrc[A_INS];
+  const u32x4* bsrc[B_INS];
+  // lane -> (row, physical chunk) of its DMA slot; it fetches the logical
+  // chunk stored there (the swizzle is an involution)
 #pragma unroll
-  for (int i = 0; i < Cfg::kALoads; ++i) {
-    const int q = tid + i * Cfg::kThreads;
-    const int r = q / CH, c = q % CH;
+  for (int i = 0; i < A_INS; ++i) {
+    const int r = RPI * (wave + NW * i) + lane / CH;
+    const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const int s = min(m0 + r, seg1 - 1);
     const int src = perm_row ? perm_row[s] : s;
-    aptr[i] = reinterpret_cast<const u32x4*>(A) + (size_t)src * kvec + c;
+    asrc[i] = A4 + (size_t)src * kvec + c;
   }
 #pragma unroll
-  for (int i = 0; i < Cfg::kBLoads; ++i) {
-    const int q = tid + i * Cfg::kThreads;
-    const int r = q / CH, c = q % CH;
+  for (int i = 0; i < B_INS; ++i) {
+    const int r = RPI * (wave + NW * i) + lane / CH;
+    const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const uint16_t* base;
     int n;
     if (SWIGLU) {
@@ -159,31 +231,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       n = c0 + r;
     }
     n = min(n, N0 - 1);
-    bptr[i] = reinterpret_cast<const u32x4*>(base) + ((size_t)e * N0 + n) * kvec + c;
+    bsrc[i] = reinterpret_cast<const u32x4*>(base) + ((size_t)e * N0 + n) * kvec + c;
   }
 
-  // LDS slot (16-byte units) of each staged chunk: row r, chunk c -> r*8 + (c ^ (r & 7))
-  int a_lds[Cfg::kALoads], b_lds[Cfg::kBLoads];
-#pragma unroll
-  for (int i = 0; i < Cfg::kALoads; ++i) {
-    const int q = tid + i * Cfg::kThreads;
-    const int r = q / CH, c = q % CH;
-    a_lds[i] = r * CH + (c ^ (r & 7));
-  }
-#pragma unroll
-  for (int i = 0; i < Cfg::kBLoads; ++i) {
-    const int q = tid + i * Cfg::kThreads;
-    const int r = q / CH, c = q % CH;
-    b_lds[i] = r * CH + (c ^ (r & 7));
-  }
-
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * Cfg::kWaveRows;
   const int li = lane & 31, lk = lane >> 5;
-  // LDS slots of the MFMA fragments for k-step 0 (k-step ks adds 2*ks to the
-  // chunk, i.e. XORs 2*ks into the swizzled chunk index)
   int fa_row[Cfg::TM], fb_row[Cfg::TN];
 #pragma unroll
   for (int tm = 0; tm < Cfg::TM; ++tm) fa_row[tm] = arow0 + tm * 32 + li;
@@ -207,58 +260,45 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / Cfg::kBK;
-  u32x4 ra[Cfg::kALoads], rb[Cfg::kBLoads];
+  const int KT = K / BK;
 #pragma unroll
-  for (int i = 0; i < Cfg::kALoads; ++i) ra[i] = aptr[i][0];
-#pragma unroll
-  for (int i = 0; i < Cfg::kBLoads; ++i) rb[i] = bptr[i][0];
-#pragma unroll
-  for (int i = 0; i < Cfg::kALoads; ++i) As[0][a_lds[i]] = ra[i];
-#pragma unroll
-  for (int i = 0; i < Cfg::kBLoads; ++i) Bs[0][b_lds[i]] = rb[i];
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const size_t off = (size_t)(kt + 1) * CH;
-#pragma unroll
-      for (int i = 0; i < Cfg::kALoads; ++i) ra[i] = aptr[i][off];
-#pragma unroll
-      for (int i = 0; i < Cfg::kBLoads; ++i) rb[i] = bptr[i][off];
+  for (int p = 0; p < NS - 1; ++p) {
+    if (p < KT) {
+      dma_slice<A_INS, NW, RPI, CH>(asrc, As[p], wave, (size_t)p * CH);
+      dma_slice<B_INS, NW, RPI, CH>(bsrc, Bs[p], wave, (size_t)p * CH);
     }
-    const u32x4* as = As[cur];
-    const u32x4* bs = Bs[cur];
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    // slice kt has landed once at most the later slices' DMAs are in flight
+    if (kt + NS - 2 < KT) MOE_WAIT_VMCNT((NS - 2) * LPS);
+    else MOE_WAIT_VMCNT(0);
+    wg_barrier();  // every wave's part of slice kt is in LDS; slice kt-1 is consumed
+    const int nx = kt + NS - 1;
+    if (nx < KT) {
+      const int sb = nx % NS;
+      dma_slice<A_INS, NW, RPI, CH>(asrc, As[sb], wave, (size_t)nx * CH);
+      dma_slice<B_INS, NW, RPI, CH>(bsrc, Bs[sb], wave, (size_t)nx * CH);
+    }
+    const u32x4* as = As[kt % NS];
+    const u32x4* bs = Bs[kt % NS];
 #pragma unroll
-    for (int ks = 0; ks < Cfg::kBK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
       const int ch = ks * 2 + lk;
       bf16x8 fa[Cfg::TM], fb[Cfg::TN];
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
-        fa[tm] = __builtin_bit_cast(bf16x8, as[fa_row[tm] * CH + (ch ^ (fa_row[tm] & 7))]);
+        fa[tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn)
-        fb[tn] = __builtin_bit_cast(bf16x8, bs[fb_row[tn] * CH + (ch ^ (fb_row[tn] & 7))]);
+        fb[tn] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
 #pragma unroll
       for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < Cfg::TN; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
     }
-    if (more) {
-      u32x4* asn = As[cur ^ 1];
-      u32x4* bsn = Bs[cur ^ 1];
-#pragma unroll
-      for (int i = 0; i < Cfg::kALoads; ++i) asn[a_lds[i]] = ra[i];
-#pragma unroll
-      for (int i = 0; i < Cfg::kBLoads; ++i) bsn[b_lds[i]] = rb[i];
-    }
-    __syncthreads();
   }
 
-  // epilogue: lane holds column (lane & 31) and rows (r&3) + 4*(lane>>5) + 8*(r>>2)
 #pragma unroll
   for (int tm = 0; tm < Cfg::TM; ++tm) {
 #pragma unroll
@@ -385,10 +425,12 @@ inline unsigned grid_for(int64_t tiles) {
   return (unsigned)(ceil_div(std::max<int64_t>(tiles, 1), kXcd) * kXcd);
 }
 
-// gate/up: BM x BN = 128 x 128 B rows (64 F columns), 2 x 2 wavefronts
-constexpr int kUpBM = 128, kUpBN = 128, kUpWM = 2, kUpWN = 2;
-// down: 128 x 128, 2 x 2 wavefronts
-constexpr int kDnBM = 128, kDnBN = 128, kDnWM = 2, kDnWN = 2;
+// Tile shape of both launches: 256 x 256 (for gate/up, 128 gate + 128 up B
+// rows = 128 F columns), 64-wide K slices, 8 wavefronts as 4 x 2 (64 x 128
+// each), 2 LDS stages (128 KiB of the CU's 160 KiB). 256 x 256 is the
+// smallest tile whose LDS fill rate (BM*BN/(BM+BN) = 128 flop per byte)
+// lets the L2 keep up with the MFMA peak.
+constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNS = 2;
 
 moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
   if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || F < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
@@ -413,10 +455,10 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
   if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h) return MOE_ERR_ARG;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
-    constexpr int kOut = kUpBN / 2;
-    const int64_t tiles = mtile_upper(rows, E, kUpBM) * ceil_div(F, kOut);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kUpBM, kUpBN, kUpWM, kUpWN, true>), dim3(grid_for(tiles)),
-                       dim3(kUpWM * kUpWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
+    constexpr int kOut = kBN / 2;
+    const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kOut);
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, true>), dim3(grid_for(tiles)),
+                       dim3(kWM * kWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
                        perm_row, expert_off, E, static_cast<const uint16_t*>(w_gate),
                        static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h));
   } else {
@@ -439,9 +481,9 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
   if (!h || !expert_off || !w_down || !y) return MOE_ERR_ARG;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
-    const int64_t tiles = mtile_upper(rows, E, kDnBM) * ceil_div(d, kDnBN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kDnBM, kDnBN, kDnWM, kDnWN, false>),
-                       dim3(grid_for(tiles)), dim3(kDnWM * kDnWN * kWave), 0, stream,
+    const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, false>),
+                       dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
                        static_cast<const uint16_t*>(h), nullptr, expert_off, E,
                        static_cast<const uint16_t*>(w_down), nullptr, F, d,
                        static_cast<uint16_t*>(y));
