@@ -123,6 +123,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14))
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -139,6 +141,23 @@ __device__ __forceinline__ void dma16(const u32x4* gptr, uint32_t lds_base) {
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_base)
+      : "memory");
+}
+
+// L2 prefetch of one 128-byte line per lane: a 4-byte direct-to-LDS load
+// whose data lands in a per-wave scratch window of LDS and is never read.
+// (A load into a VGPR would leave a late write to a register the compiler
+// may have reused.) It counts in vmcnt like the slice loads.
+__device__ __forceinline__ void prefetch_line(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(gptr), "s"(lds_base)
@@ -170,23 +189,33 @@ __device__ __forceinline__ void dma_slice(const u32x4* const (&src)[N], u32x4* s
           __builtin_amdgcn_readfirstlane(lds_addr(stage + (RPI * (wave + NW * i)) * CH)));
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, bool SWIGLU>
+template <int BM, int BN, int BK, int WM, int WN, int NS, int PD, bool SWIGLU>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C) {
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
-  constexpr int CH = BK / 8;            // 16-byte chunks per row of a K slice
-  constexpr int RPI = 512 / BK;         // rows filled by one 1 KiB DMA instruction
-  constexpr int A_INS = BM / RPI / NW;  // DMA instructions per wave per slice
-  constexpr int B_INS = BN / RPI / NW;
+  // With L2 prefetch (PD > 0) the waves split roles: the first NWD waves
+  // issue every slice DMA (and are the only ones that wait on vmcnt), the
+  // others issue only the prefetch lines. vmcnt completes in issue order,
+  // so a slow prefetch issued by a DMA wave would hold back the observed
+  // completion of the next slice.
+  constexpr int NWD = PD > 0 ? NW / 2 : NW;
+  constexpr int CH = BK / 8;             // 16-byte chunks per row of a K slice
+  constexpr int RPI = 512 / BK;          // rows filled by one 1 KiB DMA instruction
+  constexpr int A_INS = BM / RPI / NWD;  // DMA instructions per DMA wave per slice
+  constexpr int B_INS = BN / RPI / NWD;
   constexpr int LPS = A_INS + B_INS;
+  constexpr int PFL = PD > 0 ? (BM + BN) / ((NW - NWD) * kWave) : 0;  // prefetch lines per lane
   static_assert(BK == 32 || BK == 64, "K slice");
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA row split");
+  static_assert(BM % (RPI * NWD) == 0 && BN % (RPI * NWD) == 0, "DMA row split");
   static_assert(NS >= 2 && (NS - 2) * LPS <= 63, "pipeline depth");
+  static_assert(PD == 0 || (PFL >= 1 && PFL * (NW - NWD) * kWave == BM + BN && BK == 64),
+                "prefetch lines per lane");
   __shared__ u32x4 As[NS][BM * CH];
   __shared__ u32x4 Bs[NS][BN * CH];
+  __shared__ uint32_t pf_sink[PD > 0 ? NW * kWave : 1];
   __shared__ Sched sc;
 
   build_schedule(sc, expert_off, E, BM);
@@ -202,16 +231,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const size_t kvec = (size_t)K / 8;
   const u32x4* A4 = reinterpret_cast<const u32x4*>(A);
   const u32x4* asrc[A_INS];
   const u32x4* bsrc[B_INS];
   // lane -> (row, physical chunk) of its DMA slot; it fetches the logical
   // chunk stored there (the swizzle is an involution)
+  const bool dma_wave = wave < NWD;
+  const int dw = dma_wave ? wave : 0;  // prefetch waves compute (unused) pointers of wave 0
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = RPI * (wave + NW * i) + lane / CH;
+    const int r = RPI * (dw + NWD * i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const int s = min(m0 + r, seg1 - 1);
     const int src = perm_row ? perm_row[s] : s;
@@ -219,7 +250,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   }
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = RPI * (wave + NW * i) + lane / CH;
+    const int r = RPI * (dw + NWD * i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const uint16_t* base;
     int n;
@@ -233,6 +264,35 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     n = min(n, N0 - 1);
     bsrc[i] = reinterpret_cast<const u32x4*>(base) + ((size_t)e * N0 + n) * kvec + c;
   }
+
+  // prefetch waves: lane j of prefetch wave p owns rows q = (p*64 + j) + i*(prefetch threads)
+  // of the stacked [A rows; B rows] tile, one 128-byte line of each per slice
+  const char* pf_row[PFL > 0 ? PFL : 1];
+  uint32_t pf_lds = 0;
+  if (PD > 0 && !dma_wave) {
+#pragma unroll
+    for (int i = 0; i < PFL; ++i) {
+      const int q = (wave - NWD) * kWave + lane + i * (NW - NWD) * kWave;
+      if (q < BM) {
+        const int s = min(m0 + q, seg1 - 1);
+        pf_row[i] = reinterpret_cast<const char*>(A4 + (size_t)(perm_row ? perm_row[s] : s) * kvec);
+      } else {
+        const int r = q - BM;
+        const uint16_t* base;
+        int n;
+        if (SWIGLU) {
+          base = r < BN / 2 ? B0 : B1;
+          n = c0 + (r < BN / 2 ? r : r - BN / 2);
+        } else {
+          base = B0;
+          n = c0 + r;
+        }
+        n = min(n, N0 - 1);
+        pf_row[i] = reinterpret_cast<const char*>(base + ((size_t)e * N0 + n) * (size_t)K);
+      }
+    }
+  }
+  if (PD > 0) pf_lds = __builtin_amdgcn_readfirstlane(lds_addr(&pf_sink[wave * kWave]));
 
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * Cfg::kWaveRows;
@@ -261,43 +321,118 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = K / BK;
+  // DMA waves stream slices 0..NS-2 ahead; prefetch waves pull the lines of
+  // slices NS-1 .. NS+PD-2 towards L2 (at each later step, slice step + PD)
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) {
-    if (p < KT) {
-      dma_slice<A_INS, NW, RPI, CH>(asrc, As[p], wave, (size_t)p * CH);
-      dma_slice<B_INS, NW, RPI, CH>(bsrc, Bs[p], wave, (size_t)p * CH);
+    if (p < KT && dma_wave) {
+      dma_slice<A_INS, NWD, RPI, CH>(asrc, As[p], dw, (size_t)p * CH);
+      dma_slice<B_INS, NWD, RPI, CH>(bsrc, Bs[p], dw, (size_t)p * CH);
     }
   }
-  for (int kt = 0; kt < KT; ++kt) {
-    // slice kt has landed once at most the later slices' DMAs are in flight
-    if (kt + NS - 2 < KT) MOE_WAIT_VMCNT((NS - 2) * LPS);
-    else MOE_WAIT_VMCNT(0);
-    wg_barrier();  // every wave's part of slice kt is in LDS; slice kt-1 is consumed
-    const int nx = kt + NS - 1;
-    if (nx < KT) {
-      const int sb = nx % NS;
-      dma_slice<A_INS, NW, RPI, CH>(asrc, As[sb], wave, (size_t)nx * CH);
-      dma_slice<B_INS, NW, RPI, CH>(bsrc, Bs[sb], wave, (size_t)nx * CH);
-    }
-    const u32x4* as = As[kt % NS];
-    const u32x4* bs = Bs[kt % NS];
+  if (PD > 0 && !dma_wave) {
+    for (int p = NS - 1; p < min(NS - 1 + PD, KT); ++p)
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + lk;
-      bf16x8 fa[Cfg::TM], fb[Cfg::TN];
+      for (int i = 0; i < PFL; ++i) prefetch_line(pf_row[i] + (size_t)p * (BK * 2), pf_lds);
+  }
+  constexpr int KS = BK / 16;  // MFMA k-steps per slice
+  static_assert(KS % 2 == 0, "fragment double buffer parity");
+  // Fragments are double-buffered (set (ks & 1) holds k-step ks). The last
+  // k-step of a slice is read before the barrier and multiplied after it,
+  // so its MFMAs keep the matrix pipe busy while the barrier releases, the
+  // next DMA is issued and the next slice's first fragments are read. No
+  // wave reads a slice's LDS stage after that barrier, so 2 stages suffice.
+  // 32-row MFMA bands of this wave holding at least one real slot: bands
+  // wholly past the expert's last slot issue neither fragment reads nor
+  // MFMAs. The K loop is instantiated per count (dispatched once per tile),
+  // so the steady-state code has no per-band branches.
+  const int tm_live = max(0, min(Cfg::TM, (seg1 - (m0 + arow0) + 31) / 32));
+  bf16x8 fa[2][Cfg::TM], fb[2][Cfg::TN];
+  auto k_loop = [&](auto live_c) {
+    constexpr int LIVE = decltype(live_c)::value;
+    auto mfma_step = [&](int set) {
 #pragma unroll
-      for (int tm = 0; tm < Cfg::TM; ++tm)
-        fa[tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
-#pragma unroll
-      for (int tn = 0; tn < Cfg::TN; ++tn)
-        fb[tn] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
-#pragma unroll
-      for (int tm = 0; tm < Cfg::TM; ++tm)
+      for (int tm = 0; tm < LIVE; ++tm)
 #pragma unroll
         for (int tn = 0; tn < Cfg::TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][tm], fb[set][tn], acc[tm][tn], 0, 0, 0);
+    };
+    auto read_step = [&](const u32x4* as, const u32x4* bs, int set, int ks) {
+      if (LIVE == 0) return;
+      const int ch = ks * 2 + lk;
+#pragma unroll
+      for (int tm = 0; tm < LIVE; ++tm)
+        fa[set][tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn)
+        fb[set][tn] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
+    };
+    auto interleave = [&]() {
+      // one fragment read after each MFMA, then the remaining MFMAs
+      if (LIVE == 0) return;
+#pragma unroll
+      for (int i = 0; i < LIVE + Cfg::TN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LIVE * Cfg::TN - (LIVE + Cfg::TN), 0);
+    };
+    auto slice_ready = [&](int kt) {  // slice kt landed; every wave is done with slice kt-1
+      MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stage is refilled
+      if (dma_wave) {
+        if (kt + NS - 2 < KT) MOE_WAIT_VMCNT((NS - 2) * LPS);
+        else MOE_WAIT_VMCNT(0);
+      }
+      wg_barrier();
+    };
+    auto issue_next = [&](int kt) {  // DMA (and prefetch) of slice kt + NS - 1
+      const int nx = kt + NS - 1;
+      if (nx < KT && dma_wave) {
+        const int sb = nx % NS;
+        dma_slice<A_INS, NWD, RPI, CH>(asrc, As[sb], dw, (size_t)nx * CH);
+        dma_slice<B_INS, NWD, RPI, CH>(bsrc, Bs[sb], dw, (size_t)nx * CH);
+      }
+      if (PD > 0 && !dma_wave && nx + PD < KT) {
+#pragma unroll
+        for (int i = 0; i < PFL; ++i) prefetch_line(pf_row[i] + (size_t)(nx + PD) * (BK * 2), pf_lds);
+      }
+    };
+    auto first_steps = [&](int kt) {  // k-steps 0..KS-2 of slice kt; leaves set 1 = k-step KS-1
+      const u32x4* as = As[kt % NS];
+      const u32x4* bs = Bs[kt % NS];
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        read_step(as, bs, (ks + 1) & 1, ks + 1);
+        mfma_step(ks & 1);
+        interleave();
+      }
+    };
+
+    slice_ready(0);
+    issue_next(0);
+    read_step(As[0], Bs[0], 0, 0);
+    // steady state (no branch between the next slice's first reads and the
+    // MFMAs that hide them); the last slice is peeled off below
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+      first_steps(kt);
+      slice_ready(kt + 1);
+      issue_next(kt + 1);
+      read_step(As[(kt + 1) % NS], Bs[(kt + 1) % NS], 0, 0);
+      mfma_step(1);
+      interleave();
     }
+    first_steps(KT - 1);
+    mfma_step(1);
+  };
+  static_assert(Cfg::TM <= 4, "band-count dispatch");
+  switch (tm_live) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, (Cfg::TM >= 1 ? 1 : 0)>{}); break;
+    case 2: k_loop(std::integral_constant<int, (Cfg::TM >= 2 ? 2 : 0)>{}); break;
+    case 3: k_loop(std::integral_constant<int, (Cfg::TM >= 3 ? 3 : 0)>{}); break;
+    default: k_loop(std::integral_constant<int, Cfg::TM>{}); break;
   }
+  if (PD > 0) MOE_WAIT_VMCNT(0);  // no LDS write may land after the workgroup ends
 
 #pragma unroll
   for (int tm = 0; tm < Cfg::TM; ++tm) {
@@ -430,7 +565,7 @@ inline unsigned grid_for(int64_t tiles) {
 // each), 2 LDS stages (128 KiB of the CU's 160 KiB). 256 x 256 is the
 // smallest tile whose LDS fill rate (BM*BN/(BM+BN) = 128 flop per byte)
 // lets the L2 keep up with the MFMA peak.
-constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNS = 2;
+constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNS = 2, kPD = 0;
 
 moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
   if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || F < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
@@ -457,7 +592,7 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
   if (dt == MOE_BF16) {
     constexpr int kOut = kBN / 2;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kOut);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, true>), dim3(grid_for(tiles)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, kPD, true>), dim3(grid_for(tiles)),
                        dim3(kWM * kWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
                        perm_row, expert_off, E, static_cast<const uint16_t*>(w_gate),
                        static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h));
@@ -482,7 +617,7 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, false>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, kPD, false>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
                        static_cast<const uint16_t*>(h), nullptr, expert_off, E,
                        static_cast<const uint16_t*>(w_down), nullptr, F, d,
