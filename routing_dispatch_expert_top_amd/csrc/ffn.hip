@@ -385,23 +385,42 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       }
       wg_barrier();
     };
-    auto issue_next = [&](int kt) {  // DMA (and prefetch) of slice kt + NS - 1
+    // DMA of slice kt + NS - 1 in three parts: instructions [P0, P1) right
+    // after the barrier that frees its stage, [P1, P2) in k-step 0 and
+    // [P2, LPS) in k-step 1 of the next slice's compute, leaving the last
+    // k-steps for the loads to land. Issuing all of them in one burst after
+    // the barrier stalls the wave's instruction stream and costs ~10%.
+    constexpr int P1 = (LPS + 2) / 3, P2 = P1 + (LPS - P1 + 1) / 2;
+    auto issue_part = [&](int kt, int lo, int hi) {
       const int nx = kt + NS - 1;
       if (nx < KT && dma_wave) {
         const int sb = nx % NS;
-        dma_slice<A_INS, NWD, RPI, CH>(asrc, As[sb], dw, (size_t)nx * CH);
-        dma_slice<B_INS, NWD, RPI, CH>(bsrc, Bs[sb], dw, (size_t)nx * CH);
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+          if (i < lo || i >= hi) continue;
+          if (i < A_INS)
+            dma16(asrc[i] + (size_t)nx * CH,
+                  __builtin_amdgcn_readfirstlane(lds_addr(As[sb] + (RPI * (dw + NWD * i)) * CH)));
+          else
+            dma16(bsrc[i - A_INS] + (size_t)nx * CH,
+                  __builtin_amdgcn_readfirstlane(
+                      lds_addr(Bs[sb] + (RPI * (dw + NWD * (i - A_INS))) * CH)));
+        }
       }
-      if (PD > 0 && !dma_wave && nx + PD < KT) {
+      if (PD > 0 && lo == 0 && !dma_wave && nx + PD < KT) {
 #pragma unroll
         for (int i = 0; i < PFL; ++i) prefetch_line(pf_row[i] + (size_t)(nx + PD) * (BK * 2), pf_lds);
       }
     };
+    auto issue_next = [&](int kt) { issue_part(kt, 0, LPS); };
     auto first_steps = [&](int kt) {  // k-steps 0..KS-2 of slice kt; leaves set 1 = k-step KS-1
       const u32x4* as = As[kt % NS];
       const u32x4* bs = Bs[kt % NS];
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
+        // remaining parts of the DMA issued at the barrier of slice kt (it targets slice kt+NS-1)
+        if (ks == 0) issue_part(kt, P1, P2);
+        if (ks == 1) issue_part(kt, P2, LPS);
         read_step(as, bs, (ks + 1) & 1, ks + 1);
         mfma_step(ks & 1);
         interleave();
@@ -409,14 +428,14 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     };
 
     slice_ready(0);
-    issue_next(0);
+    issue_part(0, 0, P1);
     read_step(As[0], Bs[0], 0, 0);
     // steady state (no branch between the next slice's first reads and the
     // MFMAs that hide them); the last slice is peeled off below
     for (int kt = 0; kt + 1 < KT; ++kt) {
       first_steps(kt);
       slice_ready(kt + 1);
-      issue_next(kt + 1);
+      issue_part(kt + 1, 0, P1);
       read_step(As[(kt + 1) % NS], Bs[(kt + 1) % NS], 0, 0);
       mfma_step(1);
       interleave();
