@@ -30,7 +30,8 @@
  *    rank outside [0,G), NaN logits) cannot be seen by the host and give
  *    unspecified (but in-bounds) results.
  *  - Limits: 0 <= T, 1 <= k <= 16, k <= E <= 256, 1 <= G <= 32,
- *    T*k < 2^31. For the expert FFN d and F must be multiples of 64.
+ *    T*k < 2^31. For the expert FFN d and F must be multiples of 64 and the
+ *    FFN's tensors 16-byte aligned (else MOE_ERR_UNSUPPORTED).
  */
 #ifndef MOE_H
 #define MOE_H

@@ -213,8 +213,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   static_assert(NS >= 2 && (NS - 2) * LPS <= 63, "pipeline depth");
   static_assert(PD == 0 || (PFL >= 1 && PFL * (NW - NWD) * kWave == BM + BN && BK == 64),
                 "prefetch lines per lane");
-  __shared__ u32x4 As[NS][BM * CH];
-  __shared__ u32x4 Bs[NS][BN * CH];
+  // one LDS ring buffer: NS stages of A rows then NS stages of B rows; after
+  // the K loop it holds the output tile for the coalesced write-back
+  __shared__ u32x4 ring[NS * (BM + BN) * CH];
+  u32x4 (*As)[BM * CH] = reinterpret_cast<u32x4 (*)[BM * CH]>(ring);
+  u32x4 (*Bs)[BN * CH] = reinterpret_cast<u32x4 (*)[BN * CH]>(ring + NS * BM * CH);
+  static_assert(BM * Cfg::kOutCols * 2 <= NS * (BM + BN) * CH * 16, "output tile fits the ring");
   __shared__ uint32_t pf_sink[PD > 0 ? NW * kWave : 1];
   __shared__ Sched sc;
 
@@ -355,7 +359,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       for (int tm = 0; tm < LIVE; ++tm)
 #pragma unroll
         for (int tn = 0; tn < Cfg::TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][tm], fb[set][tn], acc[tm][tn], 0, 0, 0);
+          // B fragment as the first operand: the result is the transposed
+          // tile (rows = output columns, columns = slots), so each lane ends
+          // with 4 consecutive output columns of one slot per register quad
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][tn], fa[set][tm], acc[tm][tn], 0, 0, 0);
     };
     auto read_step = [&](const u32x4* as, const u32x4* bs, int set, int ks) {
       if (LIVE == 0) return;
@@ -453,27 +460,71 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   }
   if (PD > 0) MOE_WAIT_VMCNT(0);  // no LDS write may land after the workgroup ends
 
+  // Epilogue. Each lane owns slot row (lane & 31) of each 32-row band and,
+  // per register quad q, output columns 8q + 4*(lane>>5) + 0..3 of a 32-wide
+  // column tile: 4 consecutive bf16 = one 8-byte piece.
+  //  gate/up: SwiGLU, then each piece goes straight to h (h is small; no
+  //           workgroup-wide barrier at the tile end).
+  //  down:    pieces go into a row-major tile in the (now free) LDS ring with
+  //           16-byte chunks XOR-swizzled by row, and the workgroup writes y
+  //           out row by row, 16 bytes per lane (fully coalesced: y is the
+  //           bigger output and scattered 8-byte stores cost more there).
+  if (SWIGLU) {
+    constexpr int half = Cfg::TN / 2;
 #pragma unroll
-  for (int tm = 0; tm < Cfg::TM; ++tm) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + arow0 + tm * 32 + (r & 3) + 4 * lk + 8 * (r >> 2);
+    for (int tm = 0; tm < Cfg::TM; ++tm) {
+      const int row = m0 + arow0 + tm * 32 + li;
       if (row >= seg1) continue;
-      if (SWIGLU) {
-        constexpr int half = Cfg::TN / 2;
+      uint16_t* crow = C + (size_t)row * N0;
 #pragma unroll
-        for (int tg = 0; tg < half; ++tg) {
-          const int col = c0 + wn * (Cfg::kWaveCols / 2) + tg * 32 + li;
-          if (col < N0)
-            C[(size_t)row * N0 + col] = f32_to_bf16(silu_mul(acc[tm][tg][r], acc[tm][tg + half][r]));
-        }
-      } else {
+      for (int tg = 0; tg < half; ++tg) {
 #pragma unroll
-        for (int tn = 0; tn < Cfg::TN; ++tn) {
-          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + li;
-          if (col < N0) C[(size_t)row * N0 + col] = f32_to_bf16(acc[tm][tn][r]);
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = c0 + wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * lk;
+          if (col >= N0) continue;
+          const f32x16& u = acc[tm][tg];
+          const f32x16& v = acc[tm][tg + half];
+          uint2 pk;
+          pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
+          pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
+          *reinterpret_cast<uint2*>(crow + col) = pk;
         }
       }
+    }
+  } else {
+    constexpr int OC = Cfg::kOutCols;  // output columns per tile
+    constexpr int CPR = OC / 8;        // 16-byte chunks per output row
+    static_assert(CPR == 16 || CPR == 32, "output row chunks");
+    MOE_WAIT_LGKM0();  // every wave's last fragment reads are done: the ring is free
+    wg_barrier();
+    char* ot = reinterpret_cast<char*>(ring);
+    auto ot_addr = [&](int row, int col) {  // byte address of (row, col) in the tile
+      return row * (OC * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col & 7) << 1);
+    };
+#pragma unroll
+    for (int tm = 0; tm < Cfg::TM; ++tm) {
+      const int row = arow0 + tm * 32 + li;
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
+          const f32x16& a = acc[tm][tn];
+          uint2 pk;
+          pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
+          pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
+          *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
+        }
+      }
+    }
+    __syncthreads();
+    const int rows_here = min(BM, seg1 - m0);
+    for (int q = tid; q < rows_here * CPR; q += Cfg::kThreads) {
+      const int row = q / CPR, c = q % CPR;
+      const int col = c0 + c * 8;
+      if (col >= N0) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + ot_addr(row, c * 8));
+      *reinterpret_cast<u32x4*>(C + (size_t)(m0 + row) * N0 + col) = v;
     }
   }
 }
@@ -607,6 +658,8 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h) return MOE_ERR_ARG;
+  if (((uintptr_t)x_disp | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)h) % 16)
+    return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
     constexpr int kOut = kBN / 2;
@@ -633,6 +686,7 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!h || !expert_off || !w_down || !y) return MOE_ERR_ARG;
+  if (((uintptr_t)h | (uintptr_t)w_down | (uintptr_t)y) % 16) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
