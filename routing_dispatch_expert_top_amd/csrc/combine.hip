@@ -3,67 +3,113 @@
 // combined). out[t] = sum_j gates[t,j] * y[slot_of[t*k+j]], fp32 accumulation
 // in j order, stored in the activation type.
 //
-// gfx950 mapping: one wavefront per token gathers its k expert rows with
-// 16-byte loads per lane (a row is contiguous, so each load instruction is a
-// fully used 1 KiB segment), issuing all k loads of a chunk before
-// accumulating, and writes the output row once.
+// gfx950 mapping: one wavefront per token. The token's k slots and gates are
+// wave-uniform and come in through scalar loads (SGPRs); each lane then
+// gathers 16-byte chunks of the k expert rows (a row is contiguous, so each
+// load instruction is a fully used 1 KiB segment), with two chunks per lane
+// in flight per row, and writes the output row once. k is a template
+// parameter for the common values so the row loads fully unroll.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
+__device__ __forceinline__ void accum(float (&acc)[8], const u32x4& v, float g) {
+  if (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(g, bf16lo(v[q]), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(g, bf16hi(v[q]), acc[2 * q + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(v[q]), acc[q]);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack(const float (&acc)[8]) {
+  if (BF16)
+    return u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  return u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+               __float_as_uint(acc[3])};
+}
+
+// KK > 0: k == KK at compile time; KK == 0: runtime k <= kMaxK.
+template <bool BF16, int KK>
+__global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gates, int T,
-                                                      int k, int row_vecs,
-                                                      uint4* __restrict__ out) {
+                                                      int k_rt, int row_vecs,
+                                                      u32x4* __restrict__ out) {
+  constexpr int KM = KK > 0 ? KK : kMaxK;
+  const int k = KK > 0 ? KK : k_rt;
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * (blockDim.x / kWave) + wave;  // wave-uniform
   if (t >= T) return;
-  int slot[kMaxK];
-  float g[kMaxK];
+  const u32x4* rows[KM];
+  float g[KM];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    slot[j] = j < k ? slot_of[(size_t)t * k + j] : 0;
-    g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
-  }
-  for (int c = lane; c < row_vecs; c += kWave) {
-    uint4 v[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) v[j] = y[(size_t)slot[j] * row_vecs + c];
-    if (BF16) {
-      float acc[8] = {};
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-          const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] = fmaf(g[j], bf16lo(w[q]), acc[2 * q]);
-            acc[2 * q + 1] = fmaf(g[j], bf16hi(w[q]), acc[2 * q + 1]);
-          }
-        }
-      }
-      out[(size_t)t * row_vecs + c] =
-          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    } else {
-      float acc[4] = {};
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-          acc[0] = fmaf(g[j], __uint_as_float(v[j].x), acc[0]);
-          acc[1] = fmaf(g[j], __uint_as_float(v[j].y), acc[1]);
-          acc[2] = fmaf(g[j], __uint_as_float(v[j].z), acc[2]);
-          acc[3] = fmaf(g[j], __uint_as_float(v[j].w), acc[3]);
-        }
-      }
-      out[(size_t)t * row_vecs + c] = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                                                 __float_as_uint(acc[2]), __float_as_uint(acc[3]));
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      rows[j] = y + (size_t)slot_of[(size_t)t * k + j] * row_vecs;
+      g[j] = gates[(size_t)t * k + j];
     }
   }
+  u32x4* o = out + (size_t)t * row_vecs;
+  int c = lane;
+  for (; c + kWave < row_vecs; c += 2 * kWave) {
+    u32x4 v0[KM], v1[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) {
+        v0[j] = __builtin_nontemporal_load(rows[j] + c);
+        v1[j] = __builtin_nontemporal_load(rows[j] + c + kWave);
+      }
+    float a0[8] = {}, a1[8] = {};
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) {
+        accum<BF16>(a0, v0[j], g[j]);
+        accum<BF16>(a1, v1[j], g[j]);
+      }
+    o[c] = pack<BF16>(a0);
+    o[c + kWave] = pack<BF16>(a1);
+  }
+  if (c < row_vecs) {
+    float a0[8] = {};
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) accum<BF16>(a0, __builtin_nontemporal_load(rows[j] + c), g[j]);
+    o[c] = pack<BF16>(a0);
+  }
+}
+
+template <bool BF16>
+void launch_combine(const void* y, const int32_t* slot_of, const float* gates, int T, int k,
+                    int row_vecs, void* out, hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
+  const u32x4* yy = static_cast<const u32x4*>(y);
+  u32x4* oo = static_cast<u32x4*>(out);
+#define MOE_COMBINE_CASE(KV)                                                                   \
+  case KV:                                                                                     \
+    hipLaunchKernelGGL((combine_kernel<BF16, KV>), grid, block, 0, stream, yy, slot_of, gates, \
+                       T, k, row_vecs, oo);                                                    \
+    return;
+  switch (k) {
+    MOE_COMBINE_CASE(1)
+    MOE_COMBINE_CASE(2)
+    MOE_COMBINE_CASE(4)
+    MOE_COMBINE_CASE(6)
+    MOE_COMBINE_CASE(8)
+    default:
+      hipLaunchKernelGGL((combine_kernel<BF16, 0>), grid, block, 0, stream, yy, slot_of, gates,
+                         T, k, row_vecs, oo);
+  }
+#undef MOE_COMBINE_CASE
 }
 
 }  // namespace
@@ -81,14 +127,7 @@ MOE_EXPORT moe_status moe_combine(const void* y, const int32_t* slot_of, const f
   if (((size_t)d * dtype_bytes(dt)) % 16 != 0 || (uintptr_t)y % 16 || (uintptr_t)out % 16)
     return MOE_ERR_UNSUPPORTED;
   const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);
-  const dim3 grid((unsigned)ceil_div(T, 4));
-  if (dt == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream,
-                       static_cast<const uint4*>(y), slot_of, gates, T, k, row_vecs,
-                       static_cast<uint4*>(out));
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream,
-                       static_cast<const uint4*>(y), slot_of, gates, T, k, row_vecs,
-                       static_cast<uint4*>(out));
+  if (dt == MOE_BF16) launch_combine<true>(y, slot_of, gates, T, k, row_vecs, out, stream);
+  else launch_combine<false>(y, slot_of, gates, T, k, row_vecs, out, stream);
   return launch_status();
 }

@@ -111,6 +111,12 @@ __device__ void wave_excl_scan_256(const int32_t* in, int32_t* out, int n, int32
   if (lane == kWave - 1) *total = incl;
 }
 
+// One workgroup: per-key totals over the blocks, the two exclusive scans,
+// then per-block bases. A thread owns one key and walks the blocks in chunks
+// of kScanChunk whose loads are all issued before any is used, so the walk
+// costs nblk / kScanChunk memory round trips instead of nblk.
+constexpr int kScanChunk = 8;
+
 __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__ cnt, int nblk,
                                                            int E, int G,
                                                            int32_t* __restrict__ expert_off,
@@ -120,7 +126,14 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
   const int Q = E + G;
   for (int q = threadIdx.x; q < Q; q += blockDim.x) {
     int s = 0;
-    for (int b = 0; b < nblk; ++b) s += cnt[(size_t)b * Q + q];
+    for (int b0 = 0; b0 < nblk; b0 += kScanChunk) {
+      int c[kScanChunk];
+#pragma unroll
+      for (int i = 0; i < kScanChunk; ++i)
+        c[i] = b0 + i < nblk ? cnt[(size_t)(b0 + i) * Q + q] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanChunk; ++i) s += c[i];
+    }
     tot[q] = s;
   }
   __syncthreads();
@@ -132,10 +145,16 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
     int run = off[q];
     if (q < E) expert_off[q] = run;
     else rank_off[q - E] = run;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = cnt[(size_t)b * Q + q];
-      cnt[(size_t)b * Q + q] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanChunk) {
+      int c[kScanChunk];
+#pragma unroll
+      for (int i = 0; i < kScanChunk; ++i)
+        c[i] = b0 + i < nblk ? cnt[(size_t)(b0 + i) * Q + q] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanChunk; ++i) {
+        if (b0 + i < nblk) cnt[(size_t)(b0 + i) * Q + q] = run;
+        run += c[i];
+      }
     }
   }
 }
@@ -187,36 +206,38 @@ __global__ __launch_bounds__(kBlockTok) void layout_scatter_kernel(
 }
 
 // Token-major row copy: one wavefront per token reads its row once and
-// writes it to each of the token's rows.
-__global__ __launch_bounds__(256) void dispatch_rows_kernel(const uint4* __restrict__ x, int T,
+// writes it to each of the token's rows. The token index is wave-uniform, so
+// its rank count and row list come in through scalar loads.
+__global__ __launch_bounds__(256) void dispatch_rows_kernel(const u32x4* __restrict__ x, int T,
                                                             int row_vecs, int k,
                                                             const uint32_t* __restrict__ rank_mask,
                                                             const int32_t* __restrict__ tok_rows,
-                                                            uint4* __restrict__ x_disp) {
+                                                            u32x4* __restrict__ x_disp) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * (blockDim.x / kWave) + wave;
   if (t >= T) return;
   const int n = __popc(rank_mask[t]);
-  int rows[kMaxK];
+  u32x4* dst[kMaxK];  // n <= k <= kMaxK
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i) rows[i] = i < n ? tok_rows[(size_t)t * k + i] : 0;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * row_vecs;
+  for (int i = 0; i < kMaxK; ++i)
+    if (i < n) dst[i] = x_disp + (size_t)tok_rows[(size_t)t * k + i] * row_vecs;
+  const u32x4* src = x + (size_t)t * row_vecs;
   constexpr int U = 4;
   for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave + lane;
-      if (c < row_vecs) v[u] = src[c];
+      if (c < row_vecs) v[u] = __builtin_nontemporal_load(src + c);
     }
 #pragma unroll
     for (int i = 0; i < kMaxK; ++i) {
       if (i < n) {
-        u32x4* dst = reinterpret_cast<u32x4*>(x_disp) + (size_t)rows[i] * row_vecs;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = c0 + u * kWave + lane;
-          if (c < row_vecs) dst[c] = v[u];
+          if (c < row_vecs) dst[i][c] = v[u];
         }
       }
     }
@@ -284,8 +305,8 @@ MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, in
     if (x) {
       const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);
       hipLaunchKernelGGL(dispatch_rows_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
-                         stream, static_cast<const uint4*>(x), T, row_vecs, k, rank_mask,
-                         tok_rows, static_cast<uint4*>(x_disp));
+                         stream, static_cast<const u32x4*>(x), T, row_vecs, k, rank_mask,
+                         tok_rows, static_cast<u32x4*>(x_disp));
     }
   }
   return launch_status();

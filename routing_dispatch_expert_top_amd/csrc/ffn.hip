@@ -419,7 +419,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         for (int i = 0; i < PFL; ++i) prefetch_line(pf_row[i] + (size_t)(nx + PD) * (BK * 2), pf_lds);
       }
     };
-    auto issue_next = [&](int kt) { issue_part(kt, 0, LPS); };
     auto first_steps = [&](int kt) {  // k-steps 0..KS-2 of slice kt; leaves set 1 = k-step KS-1
       const u32x4* as = As[kt % NS];
       const u32x4* bs = Bs[kt % NS];

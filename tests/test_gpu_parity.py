@@ -108,6 +108,33 @@ def test_coact_accumulates_and_repeats_bit_exactly():
             assert np.array_equal(o[key], outs[0][key]), key
 
 
+# (T, E, k, offset): the first four stay under the row-owner kernel's E*T*k
+# bound of 2^24 (one with the routing result 4 bytes off 16-byte alignment,
+# which takes its scalar-load variant; one with E = 4, whose workgroups see
+# about 4096 hits each, more than their LDS hit queue holds), the others
+# exceed it and take the LDS-triangle kernel; skewed draws make some cells
+# hot.
+COACT_SHAPES = [(3000, 64, 6, 0), (8192, 128, 8, 0), (2501, 48, 5, 1), (1 << 21, 4, 2, 0),
+                (50000, 64, 6, 0), (20000, 256, 8, 0), (9000, 256, 16, 0)]
+
+
+@pytest.mark.parametrize("T,E,k,off", COACT_SHAPES,
+                         ids=[f"T{t}_E{e}_k{k}_off{o}" for t, e, k, o in COACT_SHAPES])
+def test_coact_both_kernels(T, E, k, off):
+    print(f"case coact T={T} E={E} k={k} offset={off}", flush=True)
+    rng = np.random.default_rng(T * 1000 + E + k)
+    score = rng.random((T, E)) + np.linspace(0.0, 0.6, E)[None, :]
+    idx = np.argsort(-score, axis=1)[:, :k].astype(np.int32)
+    ref = oracle.coact(idx, E)
+    seed = rng.integers(0, 5, size=(E, E)).astype(np.int32)
+    seed = seed + seed.T
+    buf = torch.empty(T * k + off, dtype=torch.int32, device="cuda")
+    buf[off:] = dev(idx.reshape(-1))
+    got = ops.moe_coact_hist(buf[off:].view(T, k), E, coact=dev(seed))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got).astype(np.int64) - seed, ref)
+
+
 def test_combine_identity_experts_returns_input():
     """With y = the token's own row (identity experts), out = x up to rounding."""
     w = synth.with_shape(synth.workload(2), T=1500)
