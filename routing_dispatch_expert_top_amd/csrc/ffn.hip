@@ -392,10 +392,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       }
       wg_barrier();
     };
-    // DMA of slice kt + NS - 1 in three parts: instructions [P0, P1) right
+    // DMA of slice kt + NS - 1 in three parts: instructions [0, P1) right
     // after the barrier that frees its stage, [P1, P2) in k-step 0 and
     // [P2, LPS) in k-step 1 of the next slice's compute, leaving the last
-    // k-steps for the loads to land. Issuing all of them in one burst after
+    // k-steps for the loads to land (with two k-steps per slice, the last
+    // two parts both go in k-step 0). Issuing all of them in one burst after
     // the barrier stalls the wave's instruction stream and costs ~10%.
     constexpr int P1 = (LPS + 2) / 3, P2 = P1 + (LPS - P1 + 1) / 2;
     auto issue_part = [&](int kt, int lo, int hi) {
@@ -425,8 +426,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
         // remaining parts of the DMA issued at the barrier of slice kt (it targets slice kt+NS-1)
-        if (ks == 0) issue_part(kt, P1, P2);
-        if (ks == 1) issue_part(kt, P2, LPS);
+        if (ks == 0) issue_part(kt, P1, KS > 2 ? P2 : LPS);
+        if (ks == 1 && KS > 2) issue_part(kt, P2, LPS);
         read_step(as, bs, (ks + 1) & 1, ks + 1);
         mfma_step(ks & 1);
         interleave();
