@@ -110,8 +110,8 @@ struct TileCfg {
 //
 // K slices travel HBM/L2 -> LDS with
 // gfx950's 16-byte direct-to-LDS loads (global_load_lds_dwordx4: each lane's
-// 16 bytes land at wave base + 16 * lane), so no registers stage them and up
-// to NS-1 slices are in flight while the MFMAs consume another. One DMA
+// 16 bytes land at wave base + 16 * lane), so no registers stage them and
+// later slices are in flight while the MFMAs consume one. One DMA
 // instruction fills 8 LDS rows of 128 bytes; a lane picks the global chunk
 // whose swizzled slot is its own, so the LDS image is the XOR-swizzled one
 // the fragment reads expect. Waits are explicit (vmcnt = DMA instructions
@@ -147,23 +147,6 @@ __device__ __forceinline__ void dma16(const u32x4* gptr, uint32_t lds_base) {
       : "memory");
 }
 
-// L2 prefetch of one 128-byte line per lane: a 4-byte direct-to-LDS load
-// whose data lands in a per-wave scratch window of LDS and is never read.
-// (A load into a VGPR would leave a late write to a register the compiler
-// may have reused.) It counts in vmcnt like the slice loads.
-__device__ __forceinline__ void prefetch_line(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(lds_base)
-      : "memory");
-}
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
@@ -179,56 +162,44 @@ __device__ __forceinline__ int swz_ch(int r, int c) {
   return r * CH + (c ^ ((r / kRowsPer256) & (CH - 1)));
 }
 
-// DMA of one K slice: instruction i of a wave fills rows [RPI*(wave+NW*i), +RPI)
-template <int N, int NW, int RPI, int CH>
-__device__ __forceinline__ void dma_slice(const u32x4* const (&src)[N], u32x4* stage, int wave,
-                                          size_t koff) {
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    dma16(src[i] + koff,
-          __builtin_amdgcn_readfirstlane(lds_addr(stage + (RPI * (wave + NW * i)) * CH)));
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int NS, int PD, bool SWIGLU>
+// Ring stages: NSA stages of A rows and NSB stages of B rows (weights). The
+// weights get the deeper ring: they are the larger stream from HBM and
+// their misses cost the most. With NSA = 2 and NSB = 3 at 256 x 256 x 64 the
+// ring is exactly the 160 KiB of LDS of a gfx950 CU, so the tile schedule is
+// built inside the ring before the first DMA lands there.
+template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C) {
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
-  // With L2 prefetch (PD > 0) the waves split roles: the first NWD waves
-  // issue every slice DMA (and are the only ones that wait on vmcnt), the
-  // others issue only the prefetch lines. vmcnt completes in issue order,
-  // so a slow prefetch issued by a DMA wave would hold back the observed
-  // completion of the next slice.
-  constexpr int NWD = PD > 0 ? NW / 2 : NW;
-  constexpr int CH = BK / 8;             // 16-byte chunks per row of a K slice
-  constexpr int RPI = 512 / BK;          // rows filled by one 1 KiB DMA instruction
-  constexpr int A_INS = BM / RPI / NWD;  // DMA instructions per DMA wave per slice
-  constexpr int B_INS = BN / RPI / NWD;
+  constexpr int CH = BK / 8;           // 16-byte chunks per row of a K slice
+  constexpr int RPI = 512 / BK;        // rows filled by one 1 KiB DMA instruction
+  constexpr int A_INS = BM / RPI / NW;  // DMA instructions per wave per slice
+  constexpr int B_INS = BN / RPI / NW;
   constexpr int LPS = A_INS + B_INS;
-  constexpr int PFL = PD > 0 ? (BM + BN) / ((NW - NWD) * kWave) : 0;  // prefetch lines per lane
   static_assert(BK == 32 || BK == 64, "K slice");
-  static_assert(BM % (RPI * NWD) == 0 && BN % (RPI * NWD) == 0, "DMA row split");
-  static_assert(NS >= 2 && (NS - 2) * LPS <= 63, "pipeline depth");
-  static_assert(PD == 0 || (PFL >= 1 && PFL * (NW - NWD) * kWave == BM + BN && BK == 64),
-                "prefetch lines per lane");
-  // one LDS ring buffer: NS stages of A rows then NS stages of B rows; after
-  // the K loop it holds the output tile for the coalesced write-back
-  __shared__ u32x4 ring[NS * (BM + BN) * CH];
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA row split");
+  static_assert(NSA == 2 && (NSB == 2 || NSB == 3), "ring depths");
+  constexpr int kRing = (NSA * BM + NSB * BN) * CH;  // 16-byte units
+  __shared__ u32x4 ring[kRing];
   u32x4 (*As)[BM * CH] = reinterpret_cast<u32x4 (*)[BM * CH]>(ring);
-  u32x4 (*Bs)[BN * CH] = reinterpret_cast<u32x4 (*)[BN * CH]>(ring + NS * BM * CH);
-  static_assert(BM * Cfg::kOutCols * 2 <= NS * (BM + BN) * CH * 16, "output tile fits the ring");
-  __shared__ uint32_t pf_sink[PD > 0 ? NW * kWave : 1];
-  __shared__ Sched sc;
+  u32x4 (*Bs)[BN * CH] = reinterpret_cast<u32x4 (*)[BN * CH]>(ring + NSA * BM * CH);
+  static_assert(BM * Cfg::kOutCols * 2 <= kRing * 16, "output tile fits the ring");
+  static_assert(sizeof(Sched) <= kRing * 16, "schedule fits the ring");
 
-  build_schedule(sc, expert_off, E, BM);
-  const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
-  const int total = sc.mt_off[E] * NT;
-  const int tile = xcd_logical_tile(total);
-  if (tile < 0) return;
   int e, nt, mt;
-  decode_tile(sc, E, NT, tile, e, nt, mt);
+  {
+    Sched& sc = *reinterpret_cast<Sched*>(ring);
+    build_schedule(sc, expert_off, E, BM);
+    const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
+    const int total = sc.mt_off[E] * NT;
+    const int tile = xcd_logical_tile(total);
+    if (tile < 0) return;  // uniform over the workgroup
+    decode_tile(sc, E, NT, tile, e, nt, mt);
+    __syncthreads();  // every wave has its tile before the first DMA overwrites the schedule
+  }
   const int seg0 = expert_off[e], seg1 = expert_off[e + 1];
   const int m0 = seg0 + mt * BM;
   const int c0 = nt * Cfg::kOutCols;
@@ -238,15 +209,14 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const size_t kvec = (size_t)K / 8;
   const u32x4* A4 = reinterpret_cast<const u32x4*>(A);
+  // lane -> (row, physical chunk) of its DMA slot; it fetches the logical
+  // chunk stored there (the swizzle is an involution). Instruction i of a
+  // wave fills rows [RPI * (wave + NW * i), + RPI).
   const u32x4* asrc[A_INS];
   const u32x4* bsrc[B_INS];
-  // lane -> (row, physical chunk) of its DMA slot; it fetches the logical
-  // chunk stored there (the swizzle is an involution)
-  const bool dma_wave = wave < NWD;
-  const int dw = dma_wave ? wave : 0;  // prefetch waves compute (unused) pointers of wave 0
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = RPI * (dw + NWD * i) + lane / CH;
+    const int r = RPI * (wave + NW * i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const int s = min(m0 + r, seg1 - 1);
     const int src = perm_row ? perm_row[s] : s;
@@ -254,7 +224,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   }
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = RPI * (dw + NWD * i) + lane / CH;
+    const int r = RPI * (wave + NW * i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const uint16_t* base;
     int n;
@@ -268,35 +238,16 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     n = min(n, N0 - 1);
     bsrc[i] = reinterpret_cast<const u32x4*>(base) + ((size_t)e * N0 + n) * kvec + c;
   }
-
-  // prefetch waves: lane j of prefetch wave p owns rows q = (p*64 + j) + i*(prefetch threads)
-  // of the stacked [A rows; B rows] tile, one 128-byte line of each per slice
-  const char* pf_row[PFL > 0 ? PFL : 1];
-  uint32_t pf_lds = 0;
-  if (PD > 0 && !dma_wave) {
-#pragma unroll
-    for (int i = 0; i < PFL; ++i) {
-      const int q = (wave - NWD) * kWave + lane + i * (NW - NWD) * kWave;
-      if (q < BM) {
-        const int s = min(m0 + q, seg1 - 1);
-        pf_row[i] = reinterpret_cast<const char*>(A4 + (size_t)(perm_row ? perm_row[s] : s) * kvec);
-      } else {
-        const int r = q - BM;
-        const uint16_t* base;
-        int n;
-        if (SWIGLU) {
-          base = r < BN / 2 ? B0 : B1;
-          n = c0 + (r < BN / 2 ? r : r - BN / 2);
-        } else {
-          base = B0;
-          n = c0 + r;
-        }
-        n = min(n, N0 - 1);
-        pf_row[i] = reinterpret_cast<const char*>(base + ((size_t)e * N0 + n) * (size_t)K);
-      }
-    }
-  }
-  if (PD > 0) pf_lds = __builtin_amdgcn_readfirstlane(lds_addr(&pf_sink[wave * kWave]));
+  // DMA instruction i of slice kt: i < A_INS fills A rows, the rest B rows
+  auto dma_ins = [&](int i, int kt) {
+    if (i < A_INS)
+      dma16(asrc[i] + (size_t)kt * CH,
+            __builtin_amdgcn_readfirstlane(lds_addr(As[kt % NSA] + (RPI * (wave + NW * i)) * CH)));
+    else
+      dma16(bsrc[i - A_INS] + (size_t)kt * CH,
+            __builtin_amdgcn_readfirstlane(
+                lds_addr(Bs[kt % NSB] + (RPI * (wave + NW * (i - A_INS))) * CH)));
+  };
 
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * Cfg::kWaveRows;
@@ -325,27 +276,25 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = K / BK;
-  // DMA waves stream slices 0..NS-2 ahead; prefetch waves pull the lines of
-  // slices NS-1 .. NS+PD-2 towards L2 (at each later step, slice step + PD)
+  // Issue order (vmcnt counts in issue order): prologue A(0), B(0), .., B(NSB-2);
+  // then the DMA issued during slice kt is A(kt+1) followed by B(kt+NSB-1).
+  // When slice kt is needed, only B(kt+NSB-2) (NSB = 3) may still be in flight.
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) {
-    if (p < KT && dma_wave) {
-      dma_slice<A_INS, NWD, RPI, CH>(asrc, As[p], dw, (size_t)p * CH);
-      dma_slice<B_INS, NWD, RPI, CH>(bsrc, Bs[p], dw, (size_t)p * CH);
+  for (int i = 0; i < A_INS; ++i) dma_ins(i, 0);
+#pragma unroll
+  for (int p = 0; p < NSB - 1; ++p)
+    if (p < KT) {
+#pragma unroll
+      for (int i = A_INS; i < LPS; ++i) dma_ins(i, p);
     }
-  }
-  if (PD > 0 && !dma_wave) {
-    for (int p = NS - 1; p < min(NS - 1 + PD, KT); ++p)
-#pragma unroll
-      for (int i = 0; i < PFL; ++i) prefetch_line(pf_row[i] + (size_t)p * (BK * 2), pf_lds);
-  }
   constexpr int KS = BK / 16;  // MFMA k-steps per slice
   static_assert(KS % 2 == 0, "fragment double buffer parity");
   // Fragments are double-buffered (set (ks & 1) holds k-step ks). The last
   // k-step of a slice is read before the barrier and multiplied after it,
   // so its MFMAs keep the matrix pipe busy while the barrier releases, the
   // next DMA is issued and the next slice's first fragments are read. No
-  // wave reads a slice's LDS stage after that barrier, so 2 stages suffice.
+  // wave reads a slice's LDS stages after that barrier, so they can be
+  // refilled right after it.
   // 32-row MFMA bands of this wave holding at least one real slot: bands
   // wholly past the expert's last slot issue neither fragment reads nor
   // MFMAs. The K loop is instantiated per count (dispatched once per tile),
@@ -354,101 +303,112 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   bf16x8 fa[2][Cfg::TM], fb[2][Cfg::TN];
   auto k_loop = [&](auto live_c) {
     constexpr int LIVE = decltype(live_c)::value;
-    auto mfma_step = [&](int set) {
+    constexpr int NM = LIVE * Cfg::TN;  // MFMAs per k-step
+    constexpr int NR = LIVE + Cfg::TN;  // fragment reads per k-step
+    static_assert(NM >= NR || LIVE <= 1, "reads fit between the MFMAs");
+    // One k-step: the NM MFMAs on fragment set `set`, with the NR fragment
+    // reads of k-step ks_next into the other set (if rd) and the DMA
+    // instructions [lo, hi) of the slices issued during slice kt placed
+    // between them, one read and at most one or two DMAs after each MFMA.
+    // The DMA asm statements keep their place in the instruction stream, so
+    // the matrix pipe is fed while the loads issue instead of draining
+    // behind a burst of them.
+    auto kstep = [&](auto chk_c, int set, bool rd, const u32x4* as, const u32x4* bs, int ks_next,
+                     int kt, int lo, int hi) {
+      constexpr bool CHK = decltype(chk_c)::value;  // false: every target slice exists
+      const int ch = ks_next * 2 + lk;
+      const int nd = hi - lo;
+      auto read_frag = [&](int j) {
+        if (j < LIVE)
+          fa[set ^ 1][j] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[j], ch)]);
+        else
+          fb[set ^ 1][j - LIVE] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[j - LIVE], ch)]);
+      };
+      auto dma_at = [&](int j) {  // DMAs that go right after MFMA j
 #pragma unroll
-      for (int tm = 0; tm < LIVE; ++tm)
+        for (int q = 0; q < LPS; ++q) {
+          if (q >= nd) break;
+          if ((NM > 0 ? q * NM / nd : 0) != j) continue;
+          const int i = lo + q;
+          const int nx = i < A_INS ? kt + 1 : kt + NSB - 1;
+          if (!CHK || nx < KT) dma_ins(i, nx);
+        }
+      };
+      if (NM == 0) {
+        dma_at(0);
+        return;
+      }
 #pragma unroll
-        for (int tn = 0; tn < Cfg::TN; ++tn)
-          // B fragment as the first operand: the result is the transposed
-          // tile (rows = output columns, columns = slots), so each lane ends
-          // with 4 consecutive output columns of one slot per register quad
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][tn], fa[set][tm], acc[tm][tn], 0, 0, 0);
+      for (int j = 0; j < NM; ++j) {
+        const int tm = j / Cfg::TN, tn = j % Cfg::TN;
+        // B fragment as the first operand: the result is the transposed
+        // tile (rows = output columns, columns = slots), so each lane ends
+        // with 4 consecutive output columns of one slot per register quad
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][tn], fa[set][tm], acc[tm][tn], 0, 0, 0);
+        if (rd && j < NR) read_frag(j);
+        if (rd && NM < NR && j == NM - 1)
+#pragma unroll
+          for (int r = NM; r < NR; ++r) read_frag(r);
+        dma_at(j);
+      }
     };
-    auto read_step = [&](const u32x4* as, const u32x4* bs, int set, int ks) {
+    auto read_first = [&](const u32x4* as, const u32x4* bs) {  // k-step 0 of a slice into set 0
       if (LIVE == 0) return;
-      const int ch = ks * 2 + lk;
+      const int ch = lk;
 #pragma unroll
       for (int tm = 0; tm < LIVE; ++tm)
-        fa[set][tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
+        fa[0][tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn)
-        fb[set][tn] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
-    };
-    auto interleave = [&]() {
-      // one fragment read after each MFMA, then the remaining MFMAs
-      if (LIVE == 0) return;
-#pragma unroll
-      for (int i = 0; i < LIVE + Cfg::TN; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, LIVE * Cfg::TN - (LIVE + Cfg::TN), 0);
+        fb[0][tn] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
     };
     auto slice_ready = [&](int kt) {  // slice kt landed; every wave is done with slice kt-1
-      MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stage is refilled
-      if (dma_wave) {
-        if (kt + NS - 2 < KT) MOE_WAIT_VMCNT((NS - 2) * LPS);
-        else MOE_WAIT_VMCNT(0);
-      }
+      MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stages are refilled
+      if (NSB == 3 && kt + 1 < KT) MOE_WAIT_VMCNT(B_INS);
+      else MOE_WAIT_VMCNT(0);
       wg_barrier();
     };
-    // DMA of slice kt + NS - 1 in three parts: instructions [0, P1) right
-    // after the barrier that frees its stage, [P1, P2) in k-step 0 and
-    // [P2, LPS) in k-step 1 of the next slice's compute, leaving the last
-    // k-steps for the loads to land (with two k-steps per slice, the last
-    // two parts both go in k-step 0). Issuing all of them in one burst after
-    // the barrier stalls the wave's instruction stream and costs ~10%.
-    constexpr int P1 = (LPS + 2) / 3, P2 = P1 + (LPS - P1 + 1) / 2;
-    auto issue_part = [&](int kt, int lo, int hi) {
-      const int nx = kt + NS - 1;
-      if (nx < KT && dma_wave) {
-        const int sb = nx % NS;
+    // The DMA issued during slice kt (A(kt+1), then B(kt+NSB-1)) is spread
+    // evenly over KS k-steps: the last k-step of slice kt-1 (multiplied after
+    // the barrier that frees the stages) and the first KS-1 k-steps of slice
+    // kt; the last k-step is left for the loads to land.
+    auto dlo = [](int q) { return q * LPS / KS; };
+    auto middle_steps = [&](auto chk_c, int kt) {  // k-steps 0..KS-2 of slice kt; leaves set 1 = k-step KS-1
+      const u32x4* as = As[kt % NSA];
+      const u32x4* bs = Bs[kt % NSB];
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-          if (i < lo || i >= hi) continue;
-          if (i < A_INS)
-            dma16(asrc[i] + (size_t)nx * CH,
-                  __builtin_amdgcn_readfirstlane(lds_addr(As[sb] + (RPI * (dw + NWD * i)) * CH)));
-          else
-            dma16(bsrc[i - A_INS] + (size_t)nx * CH,
-                  __builtin_amdgcn_readfirstlane(
-                      lds_addr(Bs[sb] + (RPI * (dw + NWD * (i - A_INS))) * CH)));
-        }
-      }
-      if (PD > 0 && lo == 0 && !dma_wave && nx + PD < KT) {
-#pragma unroll
-        for (int i = 0; i < PFL; ++i) prefetch_line(pf_row[i] + (size_t)(nx + PD) * (BK * 2), pf_lds);
-      }
+      for (int ks = 0; ks + 1 < KS; ++ks)
+        kstep(chk_c, ks & 1, true, as, bs, ks + 1, kt, dlo(ks + 1), dlo(ks + 2));
     };
-    auto first_steps = [&](int kt) {  // k-steps 0..KS-2 of slice kt; leaves set 1 = k-step KS-1
-      const u32x4* as = As[kt % NS];
-      const u32x4* bs = Bs[kt % NS];
-#pragma unroll
-      for (int ks = 0; ks + 1 < KS; ++ks) {
-        // remaining parts of the DMA issued at the barrier of slice kt (it targets slice kt+NS-1)
-        if (ks == 0) issue_part(kt, P1, KS > 2 ? P2 : LPS);
-        if (ks == 1 && KS > 2) issue_part(kt, P2, LPS);
-        read_step(as, bs, (ks + 1) & 1, ks + 1);
-        mfma_step(ks & 1);
-        interleave();
-      }
+    auto step = [&](auto chk_c, int kt) {  // slice kt's first steps, the barrier, its last step
+      middle_steps(chk_c, kt);
+      slice_ready(kt + 1);
+      // last k-step of slice kt (set 1) while reading k-step 0 of slice kt+1
+      // into set 0 and issuing the first DMA share of slice kt+1
+      kstep(chk_c, 1, true, As[(kt + 1) % NSA], Bs[(kt + 1) % NSB], 0, kt + 1, 0, dlo(1));
     };
+    constexpr std::false_type kNoCheck{};
+    constexpr std::true_type kCheck{};
 
     slice_ready(0);
-    issue_part(0, 0, P1);
-    read_step(As[0], Bs[0], 0, 0);
-    // steady state (no branch between the next slice's first reads and the
-    // MFMAs that hide them); the last slice is peeled off below
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-      first_steps(kt);
-      slice_ready(kt + 1);
-      issue_part(kt + 1, 0, P1);
-      read_step(As[(kt + 1) % NS], Bs[(kt + 1) % NS], 0, 0);
-      mfma_step(1);
-      interleave();
+    read_first(As[0], Bs[0]);
+    {
+      // the DMA share of "k-step KS-1 of slice -1": nothing to multiply yet
+#pragma unroll
+      for (int i = 0; i < LPS; ++i)
+        if (i < dlo(1)) {
+          const int nx = i < A_INS ? 1 : NSB - 1;
+          if (nx < KT) dma_ins(i, nx);
+        }
     }
-    first_steps(KT - 1);
-    mfma_step(1);
+    // steady state: while kt + 2 < KT every slice the DMA targets exists, so
+    // the loop body has no branch; the last slices check, and the last one
+    // is peeled off
+    int kt = 0;
+    for (; kt + 2 < KT; ++kt) step(kNoCheck, kt);
+    for (; kt + 1 < KT; ++kt) step(kCheck, kt);
+    middle_steps(kCheck, KT - 1);
+    kstep(kCheck, 1, false, As[0], Bs[0], 0, KT, 0, 0);
   };
   static_assert(Cfg::TM <= 4, "band-count dispatch");
   switch (tm_live) {
@@ -458,7 +418,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     case 3: k_loop(std::integral_constant<int, (Cfg::TM >= 3 ? 3 : 0)>{}); break;
     default: k_loop(std::integral_constant<int, Cfg::TM>{}); break;
   }
-  if (PD > 0) MOE_WAIT_VMCNT(0);  // no LDS write may land after the workgroup ends
 
   // Epilogue. Each lane owns slot row (lane & 31) of each 32-row band and,
   // per register quad q, output columns 8q + 4*(lane>>5) + 0..3 of a 32-wide
@@ -632,10 +591,10 @@ inline unsigned grid_for(int64_t tiles) {
 
 // Tile shape of both launches: 256 x 256 (for gate/up, 128 gate + 128 up B
 // rows = 128 F columns), 64-wide K slices, 8 wavefronts as 4 x 2 (64 x 128
-// each), 2 LDS stages (128 KiB of the CU's 160 KiB). 256 x 256 is the
-// smallest tile whose LDS fill rate (BM*BN/(BM+BN) = 128 flop per byte)
-// lets the L2 keep up with the MFMA peak.
-constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNS = 2, kPD = 0;
+// each), 2 LDS stages of A rows and 3 of weight rows (the whole 160 KiB of
+// LDS). 256 x 256 is the smallest tile whose LDS fill rate
+// (BM*BN/(BM+BN) = 128 flop per byte) lets the L2 keep up with the MFMA peak.
+constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNSA = 2, kNSB = 3;
 
 moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
   if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || F < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
@@ -664,7 +623,7 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
   if (dt == MOE_BF16) {
     constexpr int kOut = kBN / 2;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kOut);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, kPD, true>), dim3(grid_for(tiles)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, true>), dim3(grid_for(tiles)),
                        dim3(kWM * kWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
                        perm_row, expert_off, E, static_cast<const uint16_t*>(w_gate),
                        static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h));
@@ -690,7 +649,7 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNS, kPD, false>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
                        static_cast<const uint16_t*>(h), nullptr, expert_off, E,
                        static_cast<const uint16_t*>(w_down), nullptr, F, d,
