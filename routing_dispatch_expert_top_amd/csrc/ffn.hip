@@ -74,7 +74,15 @@ __device__ __forceinline__ int xcd_logical_tile(int total) {
   return logical;
 }
 
-// tile -> (expert, n-tile, m-tile); m-tiles innermost
+// Tile order inside an expert: blocks of kMBlock m-tiles; within a block,
+// n-tiles outer and m-tiles inner. Consecutive tiles (which start close
+// together on one XCD) share a weight panel, and an activation tile comes
+// back kMBlock tiles later, while its slices are still in the XCD's L2. With
+// m-tiles innermost over a whole expert, a large expert's activation tiles
+// would come back only after all of its m-tiles, long evicted.
+constexpr int kMBlock = 4;
+
+// tile -> (expert, n-tile, m-tile)
 __device__ __forceinline__ void decode_tile(const Sched& sc, int E, int NT, int tile, int& e,
                                             int& nt, int& mt) {
   int lo = 0, hi = E - 1;  // last e with mt_off[e] * NT <= tile
@@ -86,8 +94,11 @@ __device__ __forceinline__ void decode_tile(const Sched& sc, int E, int NT, int 
   e = lo;
   const int rem = tile - sc.mt_off[e] * NT;
   const int mte = sc.mt_off[e + 1] - sc.mt_off[e];
-  nt = rem / mte;
-  mt = rem % mte;
+  const int b = rem / (kMBlock * NT);        // m-block
+  const int bm = min(kMBlock, mte - b * kMBlock);  // m-tiles in this block
+  const int within = rem - b * kMBlock * NT;
+  nt = within / bm;
+  mt = b * kMBlock + within % bm;
 }
 
 __device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }
