@@ -101,7 +101,15 @@ __device__ __forceinline__ void decode_tile(const Sched& sc, int E, int NT, int 
   mt = b * kMBlock + within % bm;
 }
 
-__device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }
+// silu(u) * v = u * v / (1 + e^-u), with the hardware exp2 and reciprocal
+// (about 1 ulp each: far below the bf16 rounding of h and the fp32 tolerance).
+// Six VALU operations instead of the ~20 of a full-precision exp and an IEEE
+// division; e^-u overflowing to inf gives -0 for large negative u, as the
+// exact value rounds to.
+__device__ __forceinline__ float silu_mul(float u, float v) {
+  const float e = __builtin_amdgcn_exp2f(-u * 1.44269504088896341f);
+  return u * v * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // ---------------------------------------------------------------- bf16 MFMA
 
@@ -139,24 +147,36 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// One 16-byte direct-to-LDS load per lane into the wave's 1 KiB LDS window at
-// lds_base. Issued as inline asm so the compiler does not add its own
-// "wait for every LDS DMA" before later LDS reads; completion is tracked by
-// the explicit vmcnt waits of the K loop (VMEM ops count in issue order, so
-// the compiler's own waits for earlier loads stay correct).
-__device__ __forceinline__ void dma16(const u32x4* gptr, uint32_t lds_base) {
+// Two 16-byte direct-to-LDS loads per lane. Global address of load j =
+// base + voff_j + (OFF + 1024 j) (base in SGPRs, voff_j a 32-bit per-lane
+// byte offset); its LDS destination = M0 + (OFF + 1024 j) + 16 * lane: the
+// immediate offset moves both addresses (checked on the device), so one M0
+// value serves a wave's run of consecutive 1 KiB LDS blocks. Issued as
+// inline asm so the compiler does not add its own "wait for every LDS DMA"
+// before later LDS reads; completion is tracked by the explicit vmcnt waits
+// of the K loop (VMEM ops count in issue order, so the compiler's own waits
+// for earlier loads stay correct). M0 is restored so the compiler's view of
+// it holds.
+template <int OFF>
+__device__ __forceinline__ void dma_pair(uint32_t voff0, uint32_t voff1, const void* base,
+                                         uint32_t m0) {
+  static_assert(OFF >= 0 && OFF + 1024 < 4096, "immediate offset range");
   uint32_t saved;
-  // M0 carries the LDS base; it is restored so the compiler's view of M0 holds
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %4\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:%5\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:%6\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(gptr), "s"(lds_base)
+      : "v"(voff0), "v"(voff1), "s"(base), "s"(m0), "i"(OFF), "i"(OFF + 1024)
       : "memory");
 }
+
+// Per-lane DMA offsets are biased by this much (and the SGPR bases lowered
+// by it), so offset - (immediate of the load) never goes below zero.
+constexpr uint32_t kDmaBias = 3072;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
@@ -218,46 +238,48 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-  const size_t kvec = (size_t)K / 8;
-  const u32x4* A4 = reinterpret_cast<const u32x4*>(A);
   // lane -> (row, physical chunk) of its DMA slot; it fetches the logical
-  // chunk stored there (the swizzle is an involution). Instruction i of a
-  // wave fills rows [RPI * (wave + NW * i), + RPI).
-  const u32x4* asrc[A_INS];
-  const u32x4* bsrc[B_INS];
+  // chunk stored there (the swizzle is an involution). DMA instruction i of
+  // a wave fills the 1 KiB block of rows [RPI * (wave * INS + i), + RPI) of
+  // its operand (INS = A_INS or B_INS), so a wave's blocks are contiguous
+  // and groups of 4 share one M0 value (immediate offsets 0..3072).
+  static_assert(A_INS % 2 == 0 && B_INS % 2 == 0 && (LPS / (BK / 16)) % 2 == 0, "DMA pairs");
+  static_assert(!SWIGLU || (BN / 2) % (B_INS * RPI) == 0, "a wave's B rows sit in one half");
+  const uint32_t krow = (uint32_t)K * 2;  // bytes per operand row
+  uint32_t aoff[A_INS], boff[B_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = RPI * (wave + NW * i) + lane / CH;
+    const int r = RPI * (wave * A_INS + i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const int s = min(m0 + r, seg1 - 1);
     const int src = perm_row ? perm_row[s] : s;
-    asrc[i] = A4 + (size_t)src * kvec + c;
+    aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
   }
+  const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = RPI * (wave + NW * i) + lane / CH;
+    const int r = RPI * (wave * B_INS + i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
-    const uint16_t* base;
-    int n;
-    if (SWIGLU) {
-      base = r < BN / 2 ? B0 : B1;
-      n = c0 + (r < BN / 2 ? r : r - BN / 2);
-    } else {
-      base = B0;
-      n = c0 + r;
-    }
-    n = min(n, N0 - 1);
-    bsrc[i] = reinterpret_cast<const u32x4*>(base) + ((size_t)e * N0 + n) * kvec + c;
+    const int n = min(c0 + (b_up ? r - BN / 2 : r), N0 - 1);
+    boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
   }
-  // DMA instruction i of slice kt: i < A_INS fills A rows, the rest B rows
-  auto dma_ins = [&](int i, int kt) {
-    if (i < A_INS)
-      dma16(asrc[i] + (size_t)kt * CH,
-            __builtin_amdgcn_readfirstlane(lds_addr(As[kt % NSA] + (RPI * (wave + NW * i)) * CH)));
-    else
-      dma16(bsrc[i - A_INS] + (size_t)kt * CH,
-            __builtin_amdgcn_readfirstlane(
-                lds_addr(Bs[kt % NSB] + (RPI * (wave + NW * (i - A_INS))) * CH)));
+  const char* a_base = reinterpret_cast<const char*>(A) - kDmaBias;
+  const char* b_base = reinterpret_cast<const char*>(b_up ? B1 : B0) +
+                       (size_t)e * N0 * krow - kDmaBias;  // expert e's panel
+  // DMA instructions i, i+1 (i even) of slice kt: i < A_INS fills A rows,
+  // the rest B rows
+  auto dma_ins2 = [&](int i, int kt) {
+    const bool is_a = i < A_INS;
+    const int ii = is_a ? i : i - A_INS;
+    const int ins = is_a ? A_INS : B_INS;
+    const u32x4* stage = is_a ? As[kt % NSA] : Bs[kt % NSB];
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        lds_addr(stage + RPI * (wave * ins + (ii & ~3)) * CH));
+    const char* base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
+    const uint32_t v0 = is_a ? aoff[ii] : boff[ii];
+    const uint32_t v1 = is_a ? aoff[ii + 1] : boff[ii + 1];
+    if ((ii & 3) == 0) dma_pair<0>(v0, v1, base, m0v);
+    else dma_pair<2048>(v0, v1, base, m0v);
   };
 
   const int wm = wave / WN, wn = wave % WN;
@@ -291,12 +313,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   // then the DMA issued during slice kt is A(kt+1) followed by B(kt+NSB-1).
   // When slice kt is needed, only B(kt+NSB-2) (NSB = 3) may still be in flight.
 #pragma unroll
-  for (int i = 0; i < A_INS; ++i) dma_ins(i, 0);
+  for (int i = 0; i < A_INS; i += 2) dma_ins2(i, 0);
 #pragma unroll
   for (int p = 0; p < NSB - 1; ++p)
     if (p < KT) {
 #pragma unroll
-      for (int i = A_INS; i < LPS; ++i) dma_ins(i, p);
+      for (int i = A_INS; i < LPS; i += 2) dma_ins2(i, p);
     }
   constexpr int KS = BK / 16;  // MFMA k-steps per slice
   static_assert(KS % 2 == 0, "fragment double buffer parity");
@@ -335,14 +357,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         else
           fb[set ^ 1][j - LIVE] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[j - LIVE], ch)]);
       };
-      auto dma_at = [&](int j) {  // DMAs that go right after MFMA j
+      auto dma_at = [&](int j) {  // DMA pairs that go right after MFMA j
+        const int np = nd / 2;
 #pragma unroll
-        for (int q = 0; q < LPS; ++q) {
-          if (q >= nd) break;
-          if ((NM > 0 ? q * NM / nd : 0) != j) continue;
-          const int i = lo + q;
+        for (int q = 0; q < LPS / 2; ++q) {
+          if (q >= np) break;
+          if ((NM > 0 ? q * NM / np : 0) != j) continue;
+          const int i = lo + 2 * q;
           const int nx = i < A_INS ? kt + 1 : kt + NSB - 1;
-          if (!CHK || nx < KT) dma_ins(i, nx);
+          if (!CHK || nx < KT) dma_ins2(i, nx);
         }
       };
       if (NM == 0) {
@@ -406,10 +429,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     {
       // the DMA share of "k-step KS-1 of slice -1": nothing to multiply yet
 #pragma unroll
-      for (int i = 0; i < LPS; ++i)
+      for (int i = 0; i < LPS; i += 2)
         if (i < dlo(1)) {
           const int nx = i < A_INS ? 1 : NSB - 1;
-          if (nx < KT) dma_ins(i, nx);
+          if (nx < KT) dma_ins2(i, nx);
         }
     }
     // steady state: while kt + 2 < KT every slice the DMA targets exists, so
@@ -607,6 +630,14 @@ inline unsigned grid_for(int64_t tiles) {
 // (BM*BN/(BM+BN) = 128 flop per byte) lets the L2 keep up with the MFMA peak.
 constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNSA = 2, kNSB = 3;
 
+// The bf16 kernel addresses its operands with 32-bit per-lane byte offsets:
+// from the activation matrix (rows x K) and from one expert's weight panel
+// (N0 x K), both plus kDmaBias, must stay below 4 GiB.
+inline bool dma_offsets_fit(int64_t a_rows, int64_t n0, int64_t k) {
+  const int64_t lim = (int64_t(1) << 32) - kDmaBias - 16;
+  return a_rows * k * 2 <= lim && n0 * k * 2 <= lim;
+}
+
 moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
   if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || F < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
   if (E > kMaxE || k > kMaxK || (int64_t)T * k >= (1ll << 31) || d % 64 || F % 64)
@@ -632,6 +663,7 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
     return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
+    if (!dma_offsets_fit(rows, F, d)) return MOE_ERR_UNSUPPORTED;
     constexpr int kOut = kBN / 2;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kOut);
     hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, true>), dim3(grid_for(tiles)),
@@ -659,6 +691,7 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
   if (((uintptr_t)h | (uintptr_t)w_down | (uintptr_t)y) % 16) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
+    if (!dma_offsets_fit(rows, d, F)) return MOE_ERR_UNSUPPORTED;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
     hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
