@@ -31,7 +31,9 @@
  *    unspecified (but in-bounds) results.
  *  - Limits: 0 <= T, 1 <= k <= 16, k <= E <= 256, 1 <= G <= 32,
  *    T*k < 2^31. For the expert FFN d and F must be multiples of 64 and the
- *    FFN's tensors 16-byte aligned (else MOE_ERR_UNSUPPORTED).
+ *    FFN's tensors 16-byte aligned; in bf16 each call's activation operand
+ *    (T*k rows) and each expert's weight matrix must be under 4 GiB - 4 KiB
+ *    (else MOE_ERR_UNSUPPORTED).
  */
 #ifndef MOE_H
 #define MOE_H

@@ -90,6 +90,12 @@ def test_ffn_and_combine_argument_errors(L):
     assert L.moe_expert_down(p, p, 4, 8, 9, 64, 64, p, 1, p, None) == ops.MOE_ERR_ARG
     assert L.moe_expert_down(None, p, 4, 8, 2, 64, 64, p, 1, p, None) == ops.MOE_ERR_ARG
     assert L.moe_grouped_ffn(p, p, p, 0, 8, 2, 64, 64, p, p, p, 1, p, p, None) == ops.MOE_OK
+    # bf16 operands addressed with 32-bit offsets: 2^20 * 8 slots x 4096 bf16
+    # activations (64 GiB) and a 2^20 x 4096 weight panel are refused up front
+    big_t = 1 << 20
+    assert L.moe_expert_gate_up(p, p, p, big_t, 8, 8, 4096, 64, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down(p, p, big_t, 8, 8, 64, 4096, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 4096, 1 << 20, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
     assert L.moe_combine(p, p, p, 4, 0, 64, 1, p, None) == ops.MOE_ERR_ARG
     assert L.moe_combine(p, p, p, 4, 2, 4, 1, p, None) == ops.MOE_ERR_UNSUPPORTED  # 8-byte rows
     assert L.moe_combine(None, p, p, 4, 2, 64, 1, p, None) == ops.MOE_ERR_ARG
