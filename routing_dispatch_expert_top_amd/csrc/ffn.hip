@@ -624,11 +624,14 @@ inline unsigned grid_for(int64_t tiles) {
 }
 
 // Tile shape of both launches: 256 x 256 (for gate/up, 128 gate + 128 up B
-// rows = 128 F columns), 64-wide K slices, 8 wavefronts as 4 x 2 (64 x 128
-// each), 2 LDS stages of A rows and 3 of weight rows (the whole 160 KiB of
-// LDS). 256 x 256 is the smallest tile whose LDS fill rate
-// (BM*BN/(BM+BN) = 128 flop per byte) lets the L2 keep up with the MFMA peak.
-constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 4, kWN = 2, kNSA = 2, kNSB = 3;
+// rows = 128 F columns), 64-wide K slices, 4 wavefronts as 2 x 2 (128 x 128
+// each, accumulators in AGPRs, one wave per SIMD), 2 LDS stages of A rows and
+// 3 of weight rows (the whole 160 KiB of LDS). 256 x 256 is the smallest tile
+// whose LDS fill rate (BM*BN/(BM+BN) = 128 flop per byte) lets the L2 keep up
+// with the MFMA peak; 128 x 128 wave tiles read a third fewer fragment bytes
+// from LDS per MFMA than 64 x 128 ones, which matters on a power-limited chip
+// (8 waves of 64 x 128 are ~1-3% slower here).
+constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 2, kWN = 2, kNSA = 2, kNSB = 3;
 
 // The bf16 kernel addresses its operands with 32-bit per-lane byte offsets:
 // from the activation matrix (rows x K) and from one expert's weight panel
