@@ -372,6 +372,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         dma_at(0);
         return;
       }
+      // nothing crosses a k-step boundary: the MFMAs of this k-step use
+      // fragments read during the previous one, so none of them waits on the
+      // reads issued here (left free, the scheduler hoists the next k-step's
+      // MFMAs right behind their reads and the wave stalls on lgkmcnt)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NM; ++j) {
         const int tm = j / Cfg::TN, tn = j % Cfg::TN;
@@ -385,6 +390,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
           for (int r = NM; r < NR; ++r) read_frag(r);
         dma_at(j);
       }
+      if (rd) {
+        // one fragment read after each MFMA, then the remaining MFMAs (or reads)
+        constexpr int NP = NM < NR ? NM : NR;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        if (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+        if (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
     auto read_first = [&](const u32x4* as, const u32x4* bs) {  // k-step 0 of a slice into set 0
       if (LIVE == 0) return;
