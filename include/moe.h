@@ -165,6 +165,35 @@ moe_status moe_combine(const void* y, const int32_t* slot_of, const float* gates
                        int32_t T, int32_t k, int32_t d, moe_dtype dt, void* out,
                        hipStream_t stream);
 
+/*
+ * Expert placement planner (host code; every pointer is HOST memory).
+ * Cobalt page, English abstract: a two-stage layout planner that co-locates
+ * frequently co-activated experts and rebalances the workload inside each
+ * node; Zyphra page, English abstract: experts selected together go to the
+ * same GPU, so the once-per-GPU dispatcher sends fewer rows.
+ *  coact  [E,E] int64: co-activation counts (e.g. moe_coact_hist summed over
+ *         steps); weights are coact[a][b] + coact[b][a], the diagonal is
+ *         ignored. Must be >= 0.
+ *  load   [E] int64: per-expert token counts (>= 0), e.g. expert_off deltas.
+ *  G ranks with E/G experts each (G | E); ranks_per_node | G groups ranks
+ *         [n*rpn, (n+1)*rpn) into node n.
+ *  Stage 1: for each rank in turn, seed with the heaviest unassigned expert
+ *         and add the unassigned expert with the most co-activation weight
+ *         to the rank's members until it holds E/G; then up to swap_passes
+ *         passes over expert pairs (a < b) in different ranks, swapping
+ *         whenever that raises the total within-rank weight.
+ *  Stage 2 (ranks_per_node > 1): inside each node, repeatedly apply the
+ *         swap between its most and least loaded ranks that most lowers the
+ *         larger of their two loads (ties: most within-rank weight kept)
+ *         while it lowers it. Experts stay in their node.
+ *  Ties go to the lower expert / rank index (deterministic).
+ *  place  [E] int32 out: rank of each expert.
+ * Limits: E <= 256, G <= 32. Bad sizes or negative counts: MOE_ERR_ARG.
+ * Runs on the calling thread; no GPU work.
+ */
+moe_status moe_plan_placement(const int64_t* coact, const int64_t* load, int32_t E, int32_t G,
+                              int32_t ranks_per_node, int32_t swap_passes, int32_t* place);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,8 @@
 """Builds libmoe.so (the HIP library behind include/moe.h) for gfx950.
 
-Each .hip source is compiled to an object in parallel with hipcc, then the
-objects are linked into ``libmoe.so`` inside the package. Only symbols marked
+Each .hip source (device kernels and their entry points) and each .cpp
+source (host-only code) is compiled to an object in parallel with hipcc,
+then the objects are linked into ``libmoe.so`` inside the package. Only symbols marked
 for export (the C ABI) are visible. Packed fp32 instructions are disabled in
 device code (-packed-fp32-ops).
 """
@@ -51,9 +52,9 @@ def _compile(src: str, extra) -> str:
 
 
 def build(extra_flags=()) -> str:
-    """Compile every csrc/*.hip and link libmoe.so; returns its path."""
+    """Compile every csrc/*.hip and csrc/*.cpp and link libmoe.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
     tmp = LIB + f".tmp{os.getpid()}"

@@ -53,6 +53,7 @@ def lib():
             "moe_grouped_ffn": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p, p, C.c_int,
                                           p, p, p]),
             "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
+            "moe_plan_placement": (C.c_int, [p, p, i32, i32, i32, i32, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -190,6 +191,27 @@ def moe_grouped_ffn(x_disp, perm_row, expert_off, T, k, w_gate, w_up, w_down, h=
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), dtype_code(x_disp), _ptr(h), _ptr(y), _stream(stream)))
     return h, y
+
+
+def moe_plan_placement(coact, load, G, ranks_per_node=1, swap_passes=8):
+    """Host call: coact [E,E] and load [E] (array-likes, converted to int64
+    host arrays; device tensors are copied to the host first) -> place [E]
+    int32 numpy array."""
+    import numpy as np
+
+    def host64(a):
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+    c, ld = host64(coact), host64(load)
+    E = ld.shape[0]
+    if c.shape != (E, E):
+        raise ValueError("coact must be [E,E] with E = len(load)")
+    place = np.empty(E, dtype=np.int32)
+    _check("moe_plan_placement", lib().moe_plan_placement(
+        c.ctypes.data, ld.ctypes.data, E, G, ranks_per_node, swap_passes, place.ctypes.data))
+    return place
 
 
 def moe_combine(y, slot_of, gates, T, k, out=None, stream=None):
