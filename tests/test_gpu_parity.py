@@ -221,3 +221,34 @@ def test_placement_invariance_full_size():
     for key in ("topk_idx", "gates", "coact", "expert_off", "slot_of", "h", "y", "out"):
         assert np.array_equal(a[key], b[key]), key
     assert b["R"] < a["R"]
+
+
+@pytest.mark.parametrize("wi,rpn", [(2, 1), (3, 8)])
+def test_planned_placement_pipeline(wi, rpn):
+    """Route and co-activation on the GPU, the native planner on the host
+    (checked against the reference planner bit for bit), then the whole layer
+    with the planned placement against the oracle; the planned placement
+    sends no more rows than the index-order one."""
+    from oracle import placement as OP
+    w = synth.with_shape(synth.workload(wi), T=1536)
+    print(f"case planned {w.name} {w.tag()} rpn={rpn}", flush=True)
+    inp = synth.make(w)
+    d_in = DevInputs(w, inp)
+    lay = ops.Layer(w.T, w.d, w.E, w.k, w.F, w.G, torch.bfloat16, "cuda", w.n_groups,
+                    w.topk_groups)
+    lay.route(d_in.logits)
+    lay.coact_hist()
+    torch.cuda.synchronize()
+    coact = host(lay.coact).astype(np.int64)
+    load = np.bincount(host(lay.topk_idx).ravel(), minlength=w.E)
+    plan = ops.moe_plan_placement(coact, load, w.G, rpn, 8)
+    assert np.array_equal(plan, OP.plan(coact, load, w.G, rpn, 8))
+    inp_p = dict(inp, place=plan)
+    ref = oracle.layer(inp_p["logits"], inp_p["x"], plan, w.G, w.k, inp_p["w_gate"],
+                       inp_p["w_up"], inp_p["w_down"], w.n_groups, w.topk_groups)
+    g = run_layer(w, DevInputs(w, inp_p))
+    assert g["R"] == ref["R"]
+    compare_exact(g, ref)
+    assert_close("out", g["out"], ref["out"], TAU[w.dtype])
+    idx = host(lay.topk_idx)
+    assert ref["R"] <= OP.dispatched_rows(idx, synth.placement(w, "contiguous"))
