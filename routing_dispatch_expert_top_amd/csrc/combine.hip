@@ -7,8 +7,9 @@
 // wave-uniform and come in through scalar loads (SGPRs); each lane then
 // gathers 16-byte chunks of the k expert rows (a row is contiguous, so each
 // load instruction is a fully used 1 KiB segment), with two chunks per lane
-// in flight per row, and writes the output row once. k is a template
-// parameter for the common values so the row loads fully unroll.
+// in flight per row, and writes the output row once; each token starts at a
+// different 1 KiB block of its rows. k is a template parameter for the
+// common values so the row loads fully unroll.
 #include "moe_internal.h"
 
 namespace moe {
@@ -38,7 +39,8 @@ __device__ __forceinline__ u32x4 pack(const float (&acc)[8]) {
 }
 
 // KK > 0: k == KK at compile time; KK == 0: runtime k <= kMaxK.
-template <bool BF16, int KK>
+// WHOLE: the row is a whole number of 1 KiB blocks (no per-lane tail test).
+template <bool BF16, int KK, bool WHOLE>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gates, int T,
@@ -60,14 +62,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     }
   }
   u32x4* o = out + (size_t)t * row_vecs;
-  int c = lane;
-  for (; c + kWave < row_vecs; c += 2 * kWave) {
+  // The row is walked in 1 KiB blocks (64 lanes x 16 bytes), two blocks per
+  // step so two loads per expert row are in flight. Token t starts at block
+  // t mod nblk and wraps around: waves working at the same moment then read
+  // different offsets of their 8 KiB-strided rows instead of all hitting the
+  // same HBM channels (a fixed start measured ~6% slower).
+  const int nblk = (row_vecs + kWave - 1) / kWave;
+  const int sb = t % nblk;
+  for (int b = 0; b < nblk; b += 2) {
+    int p0 = b + sb, p1 = b + 1 + sb;
+    if (p0 >= nblk) p0 -= nblk;
+    if (p1 >= nblk) p1 -= nblk;
+    const int c0 = p0 * kWave + lane;
+    const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
+    const bool ok0 = WHOLE || c0 < row_vecs, ok1 = (WHOLE && b + 1 < nblk) || c1 < row_vecs;
     u32x4 v0[KM], v1[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (j < k) {
-        v0[j] = __builtin_nontemporal_load(rows[j] + c);
-        v1[j] = __builtin_nontemporal_load(rows[j] + c + kWave);
+        v0[j] = ok0 ? __builtin_nontemporal_load(rows[j] + c0) : u32x4{0, 0, 0, 0};
+        v1[j] = ok1 ? __builtin_nontemporal_load(rows[j] + c1) : u32x4{0, 0, 0, 0};
       }
     float a0[8] = {}, a1[8] = {};
 #pragma unroll
@@ -76,28 +90,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
         accum<BF16>(a0, v0[j], g[j]);
         accum<BF16>(a1, v1[j], g[j]);
       }
-    o[c] = pack<BF16>(a0);
-    o[c + kWave] = pack<BF16>(a1);
-  }
-  if (c < row_vecs) {
-    float a0[8] = {};
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < k) accum<BF16>(a0, __builtin_nontemporal_load(rows[j] + c), g[j]);
-    o[c] = pack<BF16>(a0);
+    if (ok0) o[c0] = pack<BF16>(a0);
+    if (ok1) o[c1] = pack<BF16>(a1);
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool WHOLE>
 void launch_combine(const void* y, const int32_t* slot_of, const float* gates, int T, int k,
                     int row_vecs, void* out, hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
   const u32x4* yy = static_cast<const u32x4*>(y);
   u32x4* oo = static_cast<u32x4*>(out);
-#define MOE_COMBINE_CASE(KV)                                                                   \
-  case KV:                                                                                     \
-    hipLaunchKernelGGL((combine_kernel<BF16, KV>), grid, block, 0, stream, yy, slot_of, gates, \
-                       T, k, row_vecs, oo);                                                    \
+#define MOE_COMBINE_CASE(KV)                                                                  \
+  case KV:                                                                                    \
+    hipLaunchKernelGGL((combine_kernel<BF16, KV, WHOLE>), grid, block, 0, stream, yy, slot_of, \
+                       gates, T, k, row_vecs, oo);                                            \
     return;
   switch (k) {
     MOE_COMBINE_CASE(1)
@@ -106,10 +113,19 @@ void launch_combine(const void* y, const int32_t* slot_of, const float* gates, i
     MOE_COMBINE_CASE(6)
     MOE_COMBINE_CASE(8)
     default:
-      hipLaunchKernelGGL((combine_kernel<BF16, 0>), grid, block, 0, stream, yy, slot_of, gates,
-                         T, k, row_vecs, oo);
+      hipLaunchKernelGGL((combine_kernel<BF16, 0, WHOLE>), grid, block, 0, stream, yy, slot_of,
+                         gates, T, k, row_vecs, oo);
   }
 #undef MOE_COMBINE_CASE
+}
+
+template <bool BF16>
+void launch_combine(const void* y, const int32_t* slot_of, const float* gates, int T, int k,
+                    int row_vecs, void* out, hipStream_t stream) {
+  if (row_vecs % kWave == 0)
+    launch_combine<BF16, true>(y, slot_of, gates, T, k, row_vecs, out, stream);
+  else
+    launch_combine<BF16, false>(y, slot_of, gates, T, k, row_vecs, out, stream);
 }
 
 }  // namespace
