@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const u32x4* __restr
   for (int i = 0; i < kMaxK; ++i)
     if (i < n) dst[i] = x_disp + (size_t)tok_rows[(size_t)t * k + i] * row_vecs;
   const u32x4* src = x + (size_t)t * row_vecs;
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
     u32x4 v[U];
 #pragma unroll
