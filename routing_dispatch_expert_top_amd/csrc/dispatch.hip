@@ -14,15 +14,17 @@
 // 256-thread workgroup). A block sets one bit per (key, token) in LDS
 // bitmaps (key = expert or rank, 8 words of 32 tokens each) with atomicOr,
 // which commutes, so the bitmaps do not depend on timing. The stable rank of
-// a token among the block's tokens with the same key is a popcount of the
-// bits below it. Three launches:
-//   count   : per-block key counts and rank_mask;
-//   scan    : one workgroup turns the counts into per-block bases and the
-//             expert_off / rank_off prefixes (no host round trip: R stays on
-//             the device);
-//   scatter : disp_token, perm_row, slot_of and a per-token row list;
-// then a token-major copy reads each token row once and writes it to each
-// of its rows (16 bytes per lane).
+// a token among the block's tokens with the same key is the popcount of the
+// bits before it. Three launches:
+//   count : per-block key counts, the bitmaps and their per-word prefix
+//           counts (to the workspace), and rank_mask;
+//   scan  : one workgroup turns the counts into per-block bases and the
+//           expert_off / rank_off prefixes (no host round trip: R stays on
+//           the device);
+//   token : one wavefront per token finds its rows and slots from the
+//           bases and bitmaps (a lane per rank and per chosen expert),
+//           writes disp_token, perm_row and slot_of, then reads the token's
+//           row once and writes it to each of its rows (16 bytes per lane).
 #include "moe_internal.h"
 
 namespace moe {
@@ -63,19 +65,30 @@ __device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk
   return m;
 }
 
+// Per block and key q (experts 0..E-1, then ranks): cnt[b][q] = tokens of
+// block b with key q; wmask[b][q][w] = the key's bitmap word w and
+// wpre[b][q][w] = popcount of words 0..w-1 (a token's rank within the block
+// is wpre + popcount of the bits before it in its word).
 __global__ __launch_bounds__(kBlockTok) void layout_count_kernel(
     const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
-    int G, uint32_t* __restrict__ rank_mask, int32_t* __restrict__ cnt) {
+    int G, uint32_t* __restrict__ rank_mask, int32_t* __restrict__ cnt,
+    uint32_t* __restrict__ wmask, int32_t* __restrict__ wpre) {
   __shared__ BlockMasks sm;
   const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, G);
   const int t = blockIdx.x * kBlockTok + threadIdx.x;
   if (t < T) rank_mask[t] = m;
   const int Q = E + G;
+  uint32_t* wm = wmask + (size_t)blockIdx.x * Q * kWords;
+  int32_t* wp = wpre + (size_t)blockIdx.x * Q * kWords;
   for (int q = threadIdx.x; q < Q; q += blockDim.x) {
     const uint32_t* mk = q < E ? &sm.emask[q * kWords] : &sm.rmask[(q - E) * kWords];
     int c = 0;
 #pragma unroll
-    for (int w = 0; w < kWords; ++w) c += __popc(mk[w]);
+    for (int w = 0; w < kWords; ++w) {
+      wm[q * kWords + w] = mk[w];
+      wp[q * kWords + w] = c;
+      c += __popc(mk[w]);
+    }
     cnt[(size_t)blockIdx.x * Q + q] = c;
   }
 }
@@ -159,69 +172,64 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
   }
 }
 
-__global__ __launch_bounds__(kBlockTok) void layout_scatter_kernel(
+// One wavefront per token. Lane i < n handles the token's i-th rank (in
+// ascending rank order): row = base + wpre + popcount of the bits before the
+// token. Lane j < k handles choice j: its slot likewise from the expert's
+// bitmap, and the row of its expert's rank comes from the rank lane by a
+// lane shuffle. Then, if x is given, the token's row is read once (eight
+// 1 KiB blocks per step, the whole 8 KiB row at d = 4096 bf16) and written
+// to each of its rows.
+__global__ __launch_bounds__(256) void dispatch_token_kernel(
     const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
-    int G, const int32_t* __restrict__ base_in, int32_t* __restrict__ disp_token,
-    int32_t* __restrict__ perm_row, int32_t* __restrict__ slot_of,
-    int32_t* __restrict__ tok_rows) {
-  __shared__ BlockMasks sm;
-  __shared__ int32_t epre[kMaxE * kWords];
-  __shared__ int32_t rpre[kMaxG * kWords];
-  __shared__ int32_t base[kMaxE + kMaxG];
-  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, G);
-  const int Q = E + G;
-  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
-    const uint32_t* mk = q < E ? &sm.emask[q * kWords] : &sm.rmask[(q - E) * kWords];
-    int32_t* pre = q < E ? &epre[q * kWords] : &rpre[(q - E) * kWords];
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kWords; ++w) {
-      pre[w] = run;
-      run += __popc(mk[w]);
-    }
-    base[q] = base_in[(size_t)blockIdx.x * Q + q];
-  }
-  __syncthreads();
-  const int t = blockIdx.x * kBlockTok + threadIdx.x;
-  if (t >= T) return;
-  const int w = threadIdx.x >> 5;
-  const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
-  int n = 0;
-  for (uint32_t mm = m; mm; mm &= mm - 1) {
-    const int g = __ffs(mm) - 1;
-    const int row = base[E + g] + rpre[g * kWords + w] + __popc(sm.rmask[g * kWords + w] & below);
-    disp_token[row] = t;
-    tok_rows[(size_t)t * k + n++] = row;
-  }
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[(size_t)t * k + j];
-    if (e < 0 || e >= E) continue;
-    const int g = sm.place[e];
-    if (g < 0 || g >= G) continue;
-    const int row = base[E + g] + rpre[g * kWords + w] + __popc(sm.rmask[g * kWords + w] & below);
-    const int s = base[e] + epre[e * kWords + w] + __popc(sm.emask[e * kWords + w] & below);
-    perm_row[s] = row;
-    slot_of[(size_t)t * k + j] = s;
-  }
-}
-
-// Token-major row copy: one wavefront per token reads its row once and
-// writes it to each of the token's rows. The token index is wave-uniform, so
-// its rank count and row list come in through scalar loads.
-__global__ __launch_bounds__(256) void dispatch_rows_kernel(const u32x4* __restrict__ x, int T,
-                                                            int row_vecs, int k,
-                                                            const uint32_t* __restrict__ rank_mask,
-                                                            const int32_t* __restrict__ tok_rows,
-                                                            u32x4* __restrict__ x_disp) {
+    int G, const uint32_t* __restrict__ rank_mask, const int32_t* __restrict__ base,
+    const uint32_t* __restrict__ wmask, const int32_t* __restrict__ wpre,
+    int32_t* __restrict__ disp_token, int32_t* __restrict__ perm_row,
+    int32_t* __restrict__ slot_of, const u32x4* __restrict__ x, int row_vecs,
+    u32x4* __restrict__ x_disp) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = blockIdx.x * (blockDim.x / kWave) + wave;
+  const int t = blockIdx.x * (blockDim.x / kWave) + wave;  // wave-uniform
   if (t >= T) return;
-  const int n = __popc(rank_mask[t]);
+  const int Q = E + G;
+  const int b = t / kBlockTok, tl = t % kBlockTok, w = tl >> 5;
+  const uint32_t below = (1u << (tl & 31)) - 1u;
+  const int32_t* bb = base + (size_t)b * Q;
+  const uint32_t* wm = wmask + (size_t)b * Q * kWords;
+  const int32_t* wp = wpre + (size_t)b * Q * kWords;
+  const uint32_t m = rank_mask[t];
+  const int n = __popc(m);
+  // rank lanes
+  int row = 0;
+  if (lane < n) {
+    uint32_t mm = m;
+    for (int i = 0; i < lane; ++i) mm &= mm - 1;  // drop the lane lowest ranks
+    const int q = E + __ffs(mm) - 1;
+    row = bb[q] + wp[q * kWords + w] + __popc(wm[q * kWords + w] & below);
+    disp_token[row] = t;
+  }
+  // choice lanes
+  int g = -1, s = 0;
+  if (lane < k) {
+    const int e = topk_idx[(size_t)t * k + lane];
+    if (e >= 0 && e < E) {
+      const int pe = place[e];
+      if (pe >= 0 && pe < G) {
+        g = pe;
+        s = bb[e] + wp[e * kWords + w] + __popc(wm[e * kWords + w] & below);
+      }
+    }
+  }
+  const int src_lane = g >= 0 ? __popc(m & ((1u << g) - 1u)) : 0;
+  const int grow = __shfl(row, src_lane, kWave);
+  if (g >= 0) {
+    perm_row[s] = grow;
+    slot_of[(size_t)t * k + lane] = s;
+  }
+  if (!x) return;
   u32x4* dst[kMaxK];  // n <= k <= kMaxK
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i)
-    if (i < n) dst[i] = x_disp + (size_t)tok_rows[(size_t)t * k + i] * row_vecs;
+    if (i < n) dst[i] = x_disp + (size_t)__builtin_amdgcn_readlane(row, i) * row_vecs;
   const u32x4* src = x + (size_t)t * row_vecs;
   constexpr int U = 8;
   for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
@@ -248,14 +256,15 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Workspace {
-  size_t cnt_bytes, rows_bytes, total;
+  size_t cnt_bytes, mask_bytes, total;
 };
 inline Workspace workspace_layout(int32_t T, int32_t E, int32_t k, int32_t G) {
+  (void)k;
   Workspace w;
   const size_t nblk = (size_t)ceil_div(T, kBlockTok);
   w.cnt_bytes = align_up(nblk * (size_t)(E + G) * sizeof(int32_t));
-  w.rows_bytes = align_up((size_t)T * k * sizeof(int32_t));
-  w.total = w.cnt_bytes + w.rows_bytes;
+  w.mask_bytes = align_up(nblk * (size_t)(E + G) * kWords * sizeof(uint32_t));
+  w.total = w.cnt_bytes + 2 * w.mask_bytes;  // counts, bitmaps, word prefixes
   if (w.total == 0) w.total = kAlign;
   return w;
 }
@@ -290,24 +299,23 @@ MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, in
   }
   const Workspace ws = workspace_layout(T, E, k, G);
   if (!workspace || workspace_bytes < ws.total) return MOE_ERR_WORKSPACE;
-  int32_t* cnt = static_cast<int32_t*>(workspace);
-  int32_t* tok_rows = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws.cnt_bytes);
+  char* wsp = static_cast<char*>(workspace);
+  int32_t* cnt = reinterpret_cast<int32_t*>(wsp);
+  uint32_t* wmask = reinterpret_cast<uint32_t*>(wsp + ws.cnt_bytes);
+  int32_t* wpre = reinterpret_cast<int32_t*>(wsp + ws.cnt_bytes + ws.mask_bytes);
   const int nblk = (int)ceil_div(T, kBlockTok);
 
   if (nblk > 0)
     hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(kBlockTok), 0, stream, topk_idx, T,
-                       E, k, place, G, rank_mask, cnt);
+                       E, k, place, G, rank_mask, cnt, wmask, wpre);
   hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, nblk, E, G,
                      expert_off, rank_off);
   if (nblk > 0) {
-    hipLaunchKernelGGL(layout_scatter_kernel, dim3(nblk), dim3(kBlockTok), 0, stream, topk_idx,
-                       T, E, k, place, G, cnt, disp_token, perm_row, slot_of, tok_rows);
-    if (x) {
-      const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);
-      hipLaunchKernelGGL(dispatch_rows_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
-                         stream, static_cast<const u32x4*>(x), T, row_vecs, k, rank_mask,
-                         tok_rows, static_cast<u32x4*>(x_disp));
-    }
+    const int row_vecs = x ? (int)((size_t)d * dtype_bytes(dt) / 16) : 0;
+    hipLaunchKernelGGL(dispatch_token_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+                       stream, topk_idx, T, E, k, place, G, rank_mask, cnt, wmask, wpre,
+                       disp_token, perm_row, slot_of, static_cast<const u32x4*>(x), row_vecs,
+                       static_cast<u32x4*>(x_disp));
   }
   return launch_status();
 }
