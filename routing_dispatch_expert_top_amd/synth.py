@@ -178,6 +178,33 @@ def placement(w: Workload, kind: str = "contiguous", seed: int = 0) -> np.ndarra
     raise ValueError(kind)
 
 
+def replicas(place: np.ndarray, G: int, ranks_per_node: int, copies: int = 2,
+             seed: int = 0) -> list:
+    """Expert copies for the replica-aware layout: expert e keeps its rank
+    place[e] and gets copies - 1 more, each on a different other node (drawn
+    with the seed) at the same position inside that node. Cobalt page,
+    English abstract: expert replicas are spread over GPUs of several nodes;
+    how many and where is not stated, so this is a synthetic choice."""
+    nodes = G // ranks_per_node
+    rng = np.random.default_rng(seed)
+    out = []
+    for p in np.asarray(place).astype(np.int64):
+        home_node, pos = divmod(int(p), ranks_per_node)
+        others = [n for n in range(nodes) if n != home_node]
+        extra = rng.permutation(others)[:max(0, min(copies, nodes) - 1)] if others else []
+        out.append(sorted([int(p)] + [int(n) * ranks_per_node + pos for n in extra]))
+    return out
+
+
+def replica_masks(reps) -> np.ndarray:
+    """Per-expert rank lists -> [E] uint32 bit masks (bit g: rank g)."""
+    m = np.zeros(len(reps), np.uint32)
+    for e, rs in enumerate(reps):
+        for g in rs:
+            m[e] |= np.uint32(1) << np.uint32(g)
+    return m
+
+
 def token_clusters(w: Workload, seed: int = 0) -> np.ndarray:
     ss = np.random.SeedSequence(seed).spawn(5)
     rng = np.random.Generator(np.random.PCG64(ss[_S_CLUSTER]))
