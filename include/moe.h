@@ -128,6 +128,42 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, in
                                hipStream_t stream);
 
 /*
+ * Replica-aware dispatch layout (Cobalt page, English abstract: expert
+ * replicas on GPUs of several nodes, and a communication-aware assignment
+ * that routes each token to fewer remote nodes for the current layout).
+ * Each chosen expert may have copies on several ranks; this call first picks
+ * one rank per (token, choice), then builds the same once-per-rank layout as
+ * moe_dispatch_layout from those ranks (outputs, orders and workspace are the
+ * same; workspace size from moe_dispatch_workspace_bytes).
+ *  rep_mask [E] uint32 (device): bit g set iff rank g holds a copy of expert
+ *           e (bits >= G are ignored). Every expert a token chooses should
+ *           have a copy: a choice without one is dropped (rank_of -1,
+ *           slot_of -1, no slot and no row), and moe_combine must not be
+ *           run on such a layout.
+ *  ranks_per_node: ranks [n*rpn, (n+1)*rpn) form node n; rpn | G.
+ * Assignment, per token t (home rank t*G/T, i.e. tokens sharded in order
+ * over the ranks; home node = home rank / rpn), over its valid choices:
+ *  nodes: while choices remain, take the node holding a copy of the most
+ *         remaining choices (ties: the home node, then the lower node) and
+ *         give it every remaining choice it can serve;
+ *  ranks: inside each chosen node, in the order chosen, while its choices
+ *         remain, take the node's rank holding the most of them (ties: the
+ *         home rank, then the lower rank) and give it all it holds.
+ * Extra outputs:
+ *  rank_of   [T*k] int32: rank serving (t, j), or -1 if dropped.
+ *  node_mask [T] uint32: bit n set iff a row of t goes to node n.
+ * With one copy per expert (rep_mask[e] = 1 << place[e]) the layout equals
+ * moe_dispatch_layout's.
+ */
+moe_status moe_replica_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                              const uint32_t* rep_mask, int32_t G, int32_t ranks_per_node,
+                              const void* x, int32_t d, moe_dtype dt, int32_t* rank_of,
+                              uint32_t* node_mask, uint32_t* rank_mask, int32_t* rank_off,
+                              int32_t* disp_token, int32_t* expert_off, int32_t* perm_row,
+                              int32_t* slot_of, void* x_disp, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Expert networks, first half: for every slot s of expert e (expert_off),
  *   a = x_disp[perm_row[s]],  u = W_gate[e] a,  v = W_up[e] a,
  *   h[s] = silu(u) * v,       silu(u) = u / (1 + exp(-u)).

@@ -40,11 +40,15 @@ struct BlockMasks {
 };
 
 // Builds the block's bitmaps; returns the token's rank mask (0 if t >= T).
+// A choice's rank is place[expert], or rank_of[t * k + j] when rank_of is
+// given (replica-aware assignment).
 __device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk_idx, int T,
-                                int E, int k, const int32_t* __restrict__ place, int G) {
+                                int E, int k, const int32_t* __restrict__ place,
+                                const int32_t* __restrict__ rank_of, int G) {
   for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) sm.emask[i] = 0u;
   for (int i = threadIdx.x; i < G * kWords; i += blockDim.x) sm.rmask[i] = 0u;
-  for (int i = threadIdx.x; i < E; i += blockDim.x) sm.place[i] = place[i];
+  if (!rank_of)
+    for (int i = threadIdx.x; i < E; i += blockDim.x) sm.place[i] = place[i];
   __syncthreads();
   const int t = blockIdx.x * kBlockTok + threadIdx.x;
   const int w = threadIdx.x >> 5;
@@ -54,7 +58,7 @@ __device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk
     for (int j = 0; j < k; ++j) {
       const int e = topk_idx[(size_t)t * k + j];
       if (e < 0 || e >= E) continue;
-      const int g = sm.place[e];
+      const int g = rank_of ? rank_of[(size_t)t * k + j] : sm.place[e];
       if (g < 0 || g >= G) continue;
       atomicOr(&sm.emask[e * kWords + w], bit);
       m |= 1u << g;
@@ -71,10 +75,10 @@ __device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk
 // is wpre + popcount of the bits before it in its word).
 __global__ __launch_bounds__(kBlockTok) void layout_count_kernel(
     const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
-    int G, uint32_t* __restrict__ rank_mask, int32_t* __restrict__ cnt,
-    uint32_t* __restrict__ wmask, int32_t* __restrict__ wpre) {
+    const int32_t* __restrict__ rank_of, int G, uint32_t* __restrict__ rank_mask,
+    int32_t* __restrict__ cnt, uint32_t* __restrict__ wmask, int32_t* __restrict__ wpre) {
   __shared__ BlockMasks sm;
-  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, G);
+  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, rank_of, G);
   const int t = blockIdx.x * kBlockTok + threadIdx.x;
   if (t < T) rank_mask[t] = m;
   const int Q = E + G;
@@ -181,7 +185,8 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
 // to each of its rows.
 __global__ __launch_bounds__(256) void dispatch_token_kernel(
     const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
-    int G, const uint32_t* __restrict__ rank_mask, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ rank_of, int G, const uint32_t* __restrict__ rank_mask,
+    const int32_t* __restrict__ base,
     const uint32_t* __restrict__ wmask, const int32_t* __restrict__ wpre,
     int32_t* __restrict__ disp_token, int32_t* __restrict__ perm_row,
     int32_t* __restrict__ slot_of, const u32x4* __restrict__ x, int row_vecs,
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
   if (lane < k) {
     const int e = topk_idx[(size_t)t * k + lane];
     if (e >= 0 && e < E) {
-      const int pe = place[e];
+      const int pe = rank_of ? rank_of[(size_t)t * k + lane] : place[e];
       if (pe >= 0 && pe < G) {
         g = pe;
         s = bb[e] + wp[e * kWords + w] + __popc(wm[e * kWords + w] & below);
@@ -221,10 +226,8 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
   }
   const int src_lane = g >= 0 ? __popc(m & ((1u << g) - 1u)) : 0;
   const int grow = __shfl(row, src_lane, kWave);
-  if (g >= 0) {
-    perm_row[s] = grow;
-    slot_of[(size_t)t * k + lane] = s;
-  }
+  if (g >= 0) perm_row[s] = grow;
+  if (lane < k) slot_of[(size_t)t * k + lane] = g >= 0 ? s : -1;  // -1: dropped choice
   if (!x) return;
   u32x4* dst[kMaxK];  // n <= k <= kMaxK
 #pragma unroll
@@ -250,6 +253,79 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
       }
     }
   }
+}
+
+// Replica-aware assignment (Cobalt page, English abstract: route each token
+// to fewer remote nodes given where the expert replicas are). A greedy
+// cover per token: while choices remain, take the node holding a copy of the
+// most remaining choices (ties: the token's home node, then the lower node)
+// and give it every remaining choice it can serve; inside that node, while
+// its choices remain, take the rank holding the most of them (ties: the home
+// rank, then the lower rank) and give it all it holds. Home rank = t * G / T
+// (tokens sharded in order over the ranks). A choice whose expert is out of
+// range or has no copy gets rank -1.
+//
+// gfx950 mapping: one lane per (token, choice). A token owns a group of P
+// consecutive lanes (P = power of two >= k, at most 16), so a wavefront holds
+// 64 / P tokens and the counts of the greedy are popcounts of one wave ballot
+// masked to the group. Every decision depends only on the group's ballots,
+// so the lanes of a group always take the same branch.
+__global__ __launch_bounds__(256) void replica_assign_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int E, int k, int log_p,
+    const uint32_t* __restrict__ rep_mask, int G, int rpn, int32_t* __restrict__ rank_of,
+    uint32_t* __restrict__ node_mask) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int P = 1 << log_p;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = (int)(gt >> log_p);
+  const int j = lane & (P - 1);
+  const uint64_t grp = (P == kWave ? ~0ull : ((1ull << P) - 1ull)) << (lane & ~(P - 1));
+  const bool mine = t < T && j < k;
+  uint32_t cm = 0;
+  if (mine) {
+    const int e = topk_idx[(size_t)t * k + j];
+    if (e >= 0 && e < E) cm = rep_mask[e] & (G == 32 ? 0xFFFFFFFFu : ((1u << G) - 1u));
+  }
+  const int home = t < T ? (int)((int64_t)t * G / T) : 0;
+  const int hnode = home / rpn, nodes = G / rpn;
+  const uint32_t node0 = rpn == 32 ? 0xFFFFFFFFu : ((1u << rpn) - 1u);
+  uint64_t left = __ballot(cm != 0u) & grp;
+  int32_t rk = -1;
+  uint32_t nm = 0;
+  while (left) {
+    const bool in_left = (left >> lane) & 1ull;
+    int best = 0, bc = -1;
+    uint64_t bj = 0;
+    for (int n = 0; n < nodes; ++n) {
+      const uint64_t jm = __ballot(in_left && (cm & (node0 << (n * rpn))) != 0u) & grp;
+      const int c = __popcll(jm);
+      if (c > bc || (c == bc && n == hnode && best != hnode)) {
+        best = n;
+        bc = c;
+        bj = jm;
+      }
+    }
+    left &= ~bj;
+    nm |= 1u << best;
+    while (bj) {
+      const bool in_node = (bj >> lane) & 1ull;
+      int br = 0, brc = -1;
+      uint64_t brj = 0;
+      for (int r = best * rpn; r < (best + 1) * rpn; ++r) {
+        const uint64_t jm = __ballot(in_node && ((cm >> r) & 1u)) & grp;
+        const int c = __popcll(jm);
+        if (c > brc || (c == brc && r == home && br != home)) {
+          br = r;
+          brc = c;
+          brj = jm;
+        }
+      }
+      if ((brj >> lane) & 1ull) rk = br;
+      bj &= ~brj;
+    }
+  }
+  if (mine) rank_of[(size_t)t * k + j] = rk;
+  if (t < T && j == 0) node_mask[t] = nm;
 }
 
 constexpr size_t kAlign = 256;
@@ -279,19 +355,18 @@ MOE_EXPORT size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k, 
   return workspace_layout(T, E, k, G).total;
 }
 
-MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
-                                          const int32_t* place, int32_t G, const void* x, int32_t d,
-                                          moe_dtype dt, uint32_t* rank_mask, int32_t* rank_off,
-                                          int32_t* disp_token, int32_t* expert_off,
-                                          int32_t* perm_row, int32_t* slot_of, void* x_disp,
-                                          void* workspace, size_t workspace_bytes,
-                                          hipStream_t stream) {
-  if (T < 0 || E < 1 || k < 1 || k > E || G < 1) return MOE_ERR_ARG;
-  if (E > kMaxE || k > kMaxK || G > kMaxG || (int64_t)T * k >= (1ll << 31))
-    return MOE_ERR_UNSUPPORTED;
-  if (!place || !rank_off || !expert_off) return MOE_ERR_ARG;
+namespace moe {
+namespace {
+
+moe_status layout_impl(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                       const int32_t* place, const int32_t* rank_of, int32_t G, const void* x,
+                       int32_t d, moe_dtype dt, uint32_t* rank_mask, int32_t* rank_off,
+                       int32_t* disp_token, int32_t* expert_off, int32_t* perm_row,
+                       int32_t* slot_of, void* x_disp, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
   if (T > 0 && (!topk_idx || !rank_mask || !disp_token || !perm_row || !slot_of))
     return MOE_ERR_ARG;
+  if (!rank_off || !expert_off) return MOE_ERR_ARG;
   if (x) {
     if (!valid_dtype(dt) || d < 1 || (T > 0 && !x_disp)) return MOE_ERR_ARG;
     if (((size_t)d * dtype_bytes(dt)) % 16 != 0 || (uintptr_t)x % 16 || (uintptr_t)x_disp % 16)
@@ -307,15 +382,61 @@ MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, in
 
   if (nblk > 0)
     hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(kBlockTok), 0, stream, topk_idx, T,
-                       E, k, place, G, rank_mask, cnt, wmask, wpre);
+                       E, k, place, rank_of, G, rank_mask, cnt, wmask, wpre);
   hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, nblk, E, G,
                      expert_off, rank_off);
   if (nblk > 0) {
     const int row_vecs = x ? (int)((size_t)d * dtype_bytes(dt) / 16) : 0;
     hipLaunchKernelGGL(dispatch_token_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
-                       stream, topk_idx, T, E, k, place, G, rank_mask, cnt, wmask, wpre,
+                       stream, topk_idx, T, E, k, place, rank_of, G, rank_mask, cnt, wmask, wpre,
                        disp_token, perm_row, slot_of, static_cast<const u32x4*>(x), row_vecs,
                        static_cast<u32x4*>(x_disp));
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                          const int32_t* place, int32_t G, const void* x, int32_t d,
+                                          moe_dtype dt, uint32_t* rank_mask, int32_t* rank_off,
+                                          int32_t* disp_token, int32_t* expert_off,
+                                          int32_t* perm_row, int32_t* slot_of, void* x_disp,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || G < 1) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK || G > kMaxG || (int64_t)T * k >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (!place) return MOE_ERR_ARG;
+  return layout_impl(topk_idx, T, E, k, place, nullptr, G, x, d, dt, rank_mask, rank_off,
+                     disp_token, expert_off, perm_row, slot_of, x_disp, workspace,
+                     workspace_bytes, stream);
+}
+
+MOE_EXPORT moe_status moe_replica_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                         const uint32_t* rep_mask, int32_t G,
+                                         int32_t ranks_per_node, const void* x, int32_t d,
+                                         moe_dtype dt, int32_t* rank_of, uint32_t* node_mask,
+                                         uint32_t* rank_mask, int32_t* rank_off,
+                                         int32_t* disp_token, int32_t* expert_off,
+                                         int32_t* perm_row, int32_t* slot_of, void* x_disp,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || G < 1 || ranks_per_node < 1) return MOE_ERR_ARG;
+  if (G % ranks_per_node != 0) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK || G > kMaxG || (int64_t)T * k >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (!rep_mask || (T > 0 && (!rank_of || !node_mask))) return MOE_ERR_ARG;
+  if (T > 0) {
+    int log_p = 0;
+    while ((1 << log_p) < k) ++log_p;  // k <= kMaxK = 16, so a group fits a wave
+    const int64_t lanes = (int64_t)T << log_p;
+    hipLaunchKernelGGL(replica_assign_kernel, dim3((unsigned)ceil_div(lanes, 256)), dim3(256), 0,
+                       stream, topk_idx, T, E, k, log_p, rep_mask, G, ranks_per_node, rank_of,
+                       node_mask);
+  }
+  return layout_impl(topk_idx, T, E, k, nullptr, rank_of, G, x, d, dt, rank_mask, rank_off,
+                     disp_token, expert_off, perm_row, slot_of, x_disp, workspace,
+                     workspace_bytes, stream);
 }

@@ -54,6 +54,8 @@ def lib():
                                           p, p, p]),
             "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
             "moe_plan_placement": (C.c_int, [p, p, i32, i32, i32, i32, p]),
+            "moe_replica_layout": (C.c_int, [p, i32, i32, i32, p, i32, i32, p, i32, C.c_int,
+                                             p, p, p, p, p, p, p, p, p, p, sz, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -156,6 +158,31 @@ def moe_dispatch_layout(topk_idx, E, place, G, x=None, out=None, stream=None):
     ws = out["workspace"]
     _check("moe_dispatch_layout", lib().moe_dispatch_layout(
         _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(x), d or 0, dt,
+        _ptr(out["rank_mask"]), _ptr(out["rank_off"]), _ptr(out["disp_token"]),
+        _ptr(out["expert_off"]), _ptr(out["perm_row"]), _ptr(out["slot_of"]),
+        _ptr(out.get("x_disp")) if x is not None else None, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def moe_replica_layout(topk_idx, E, rep_mask, G, ranks_per_node, x=None, out=None,
+                       stream=None):
+    """rep_mask [E] int32 device tensor (uint32 bits: ranks holding a copy of
+    expert e). Returns the layout dict of moe_dispatch_layout plus rank_of
+    [T*k] and node_mask [T] (uint32 bits in an int32 tensor)."""
+    T, k = topk_idx.shape
+    d = x.shape[1] if x is not None else None
+    dev = topk_idx.device
+    if out is None:
+        out = alloc_layout(T, E, k, G, dev, d, x.dtype if x is not None else None)
+    if "rank_of" not in out:
+        out["rank_of"] = torch.empty(T * k, dtype=torch.int32, device=dev)
+        out["node_mask"] = torch.empty(T, dtype=torch.int32, device=dev)
+    dt = dtype_code(x) if x is not None else MOE_F32
+    ws = out["workspace"]
+    _check("moe_replica_layout", lib().moe_replica_layout(
+        _ptr(topk_idx), T, E, k, _ptr(rep_mask), G, ranks_per_node, _ptr(x), d or 0, dt,
+        _ptr(out["rank_of"]), _ptr(out["node_mask"]),
         _ptr(out["rank_mask"]), _ptr(out["rank_off"]), _ptr(out["disp_token"]),
         _ptr(out["expert_off"]), _ptr(out["perm_row"]), _ptr(out["slot_of"]),
         _ptr(out.get("x_disp")) if x is not None else None, _ptr(ws), ws.numel(),

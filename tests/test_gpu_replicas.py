@@ -1,0 +1,163 @@
+"""GPU parity of the replica-aware layout (moe_replica_layout) against the
+reference assignment and layout: bit-exact per-choice ranks, node masks, the
+whole once-per-rank layout and the dispatched rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import replicas as rep
+from routing_dispatch_expert_top_amd import ops, synth
+from tests.gpu_helpers import compare_exact, dev, host
+from tests.test_replicas import load_golden
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_KEYS = ("rank_mask", "rank_off", "disp_token", "expert_off", "perm_row", "slot_of")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+
+
+def _topk(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+
+
+def run_replica(idx, E, reps, G, rpn, x=None):
+    """moe_replica_layout on the GPU; every output downloaded."""
+    T, k = idx.shape
+    masks = synth.replica_masks(reps).view(np.int32)
+    out = ops.moe_replica_layout(dev(idx), E, dev(masks), G, rpn,
+                                 dev(x) if x is not None else None)
+    torch.cuda.synchronize()
+    R = int(out["rank_off"][G].item())
+    S = int(out["expert_off"][E].item())
+    g = dict(rank_of=host(out["rank_of"]), node_mask=host(out["node_mask"]).view(np.uint32),
+             rank_mask=host(out["rank_mask"]).view(np.uint32), rank_off=host(out["rank_off"]),
+             disp_token=host(out["disp_token"][:R]), expert_off=host(out["expert_off"]),
+             perm_row=host(out["perm_row"][:S]), slot_of=host(out["slot_of"]), R=R)
+    if x is not None:
+        g["x_disp"] = host(out["x_disp"][:R])
+    return g
+
+
+def reference(idx, E, reps, G, rpn):
+    ro = rep.assign(idx, reps, G, rpn)
+    lay = rep.layout(idx, ro, E, G)
+    st = rep.node_stats(lay["rank_mask"], G, rpn)
+    return dict(lay, rank_of=ro.reshape(-1), node_mask=st["node_mask"],
+                perm_row=lay["perm_row"], cross=st)
+
+
+def check(g, r):
+    assert g["R"] == r["R"]
+    compare_exact(g, r, LAYOUT_KEYS + ("rank_of", "node_mask"))
+
+
+CASES = [  # T, E, k, G, rpn, copies, dtype, d, seed
+    (777, 16, 4, 8, 2, 2, "bf16", 256, 0),
+    (500, 12, 3, 6, 3, 3, "f32", 192, 1),
+    (1, 8, 2, 4, 2, 2, "bf16", 64, 2),
+    (300, 64, 8, 32, 8, 4, "bf16", 128, 3),
+    (257, 32, 6, 32, 1, 3, None, 0, 4),
+    (129, 16, 16, 4, 4, 1, "bf16", 64, 5),
+    (1000, 256, 16, 32, 4, 8, "bf16", 64, 6),
+    (2049, 24, 5, 12, 6, 2, "f32", 128, 7),
+]
+
+
+@pytest.mark.parametrize("T,E,k,G,rpn,copies,dtype,d,seed", CASES)
+def test_replica_layout_parity(T, E, k, G, rpn, copies, dtype, d, seed):
+    print(f"case replica T={T} E={E} k={k} G={G} rpn={rpn} copies={copies}", flush=True)
+    idx = _topk(T, E, k, seed)
+    place = np.random.default_rng(seed + 50).permutation(np.repeat(np.arange(G), -(-E // G))[:E])
+    reps = synth.replicas(place.astype(np.int32), G, rpn, copies, seed)
+    x = None
+    if dtype is not None:
+        x32 = np.random.default_rng(seed + 9).standard_normal((T, d)).astype(np.float32)
+        x = synth.f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+    g = run_replica(idx, E, reps, G, rpn, x)
+    r = reference(idx, E, reps, G, rpn)
+    check(g, r)
+    if x is not None:
+        assert np.array_equal(g["x_disp"], oracle.dispatch_rows(x, r["disp_token"]))
+
+
+@pytest.mark.parametrize("name", ["A", "B", "C"])
+def test_replica_layout_golden(name):
+    c = load_golden()[name]
+    g = run_replica(c["topk"], c["E"], c["reps"], c["G"], c["rpn"])
+    assert g["rank_of"].tolist() == c["rank_of"]
+    assert g["node_mask"].tolist() == c["node_mask"]
+    for key in LAYOUT_KEYS:
+        if key in c:
+            assert g[key].tolist() == c[key], key
+
+
+def test_single_copy_equals_dispatch_layout():
+    T, E, k, G = 3001, 64, 6, 16
+    idx = _topk(T, E, k, 11)
+    place = np.random.default_rng(12).integers(0, G, size=E).astype(np.int32)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(13).standard_normal((T, 128)).astype(np.float32))
+    g = run_replica(idx, E, [[int(p)] for p in place], G, 4, x)
+    lay = ops.moe_dispatch_layout(dev(idx), E, dev(place), G, dev(x))
+    torch.cuda.synchronize()
+    R = int(lay["rank_off"][G].item())
+    assert g["R"] == R
+    assert np.array_equal(g["rank_of"], place[idx].reshape(-1))
+    for key in LAYOUT_KEYS:
+        want = host(lay[key])
+        want = want.view(np.uint32) if key == "rank_mask" else want
+        n = len(g[key])
+        assert np.array_equal(g[key], want[:n]), key
+    assert np.array_equal(g["x_disp"], host(lay["x_disp"][:R]))
+
+
+def test_dropped_choices():
+    T, E, k, G, rpn = 400, 16, 4, 8, 2
+    idx = _topk(T, E, k, 21)
+    reps = synth.replicas(np.arange(E, dtype=np.int32) % G, G, rpn, 2, 22)
+    reps[3] = []
+    reps[10] = []
+    g = run_replica(idx, E, reps, G, rpn)
+    r = reference(idx, E, reps, G, rpn)
+    check(g, r)
+    dropped = np.isin(idx.reshape(-1), [3, 10])
+    assert dropped.any() and (g["slot_of"][dropped] == -1).all() and (g["rank_of"][dropped] == -1).all()
+
+
+def test_empty_batch():
+    idx = np.zeros((0, 4), np.int32)
+    g = run_replica(idx, 16, [[e % 4] for e in range(16)], 4, 2)
+    assert g["R"] == 0 and g["rank_off"].tolist() == [0] * 5 and g["expert_off"].tolist() == [0] * 17
+
+
+def test_argument_errors():
+    idx = dev(_topk(16, 8, 2, 0))
+    m = dev(synth.replica_masks([[e % 4] for e in range(8)]).view(np.int32))
+    with pytest.raises(ops.MoeError):
+        ops.moe_replica_layout(idx, 8, m, 4, 3)  # rpn does not divide G
+    with pytest.raises(ops.MoeError):
+        ops.moe_replica_layout(idx, 8, m, 4, 0)
+    with pytest.raises(ops.MoeError):
+        ops.moe_replica_layout(idx, 8, m, 33, 1)  # more ranks than mask bits
+
+
+@pytest.mark.timeout(600)
+def test_full_size_replicas():
+    """T=8192, E=128, k=8, G=32 in nodes of 8, two copies per expert, routed
+    from the clustered logits of that workload, with the bf16 rows."""
+    w = synth.workload(3)
+    print(f"case replica full {w.tag()}", flush=True)
+    inp = synth.make(w, place="contiguous", with_weights=False)
+    idx, _ = oracle.route(inp["logits"], w.k, w.n_groups, w.topk_groups)
+    reps = synth.replicas(inp["place"], w.G, 8, 2, 0)
+    g = run_replica(idx, w.E, reps, w.G, 8, inp["x"])
+    r = reference(idx, w.E, reps, w.G, 8)
+    check(g, r)
+    assert np.array_equal(g["x_disp"], oracle.dispatch_rows(inp["x"], r["disp_token"]))
