@@ -205,8 +205,17 @@ def replica_masks(reps) -> np.ndarray:
     return m
 
 
-def token_clusters(w: Workload, seed: int = 0) -> np.ndarray:
-    ss = np.random.SeedSequence(seed).spawn(5)
+def _batch_streams(seed: int, batch: int):
+    """Seed streams of the per-token draws. The model structure (expert
+    clusters, cross-layer maps) depends on ``seed`` only; ``batch`` > 0 draws
+    another batch of tokens from the same model (batch 0 is the default one)."""
+    if batch == 0:
+        return np.random.SeedSequence(seed).spawn(5)
+    return np.random.SeedSequence([seed, 1000 + batch]).spawn(5)
+
+
+def token_clusters(w: Workload, seed: int = 0, batch: int = 0) -> np.ndarray:
+    ss = _batch_streams(seed, batch)
     rng = np.random.Generator(np.random.PCG64(ss[_S_CLUSTER]))
     C = w.clusters
     if w.zipf > 0:
@@ -217,21 +226,57 @@ def token_clusters(w: Workload, seed: int = 0) -> np.ndarray:
     return rng.choice(C, size=w.T, p=p).astype(np.int32)
 
 
-def logits(w: Workload, seed: int = 0, hot_bias: float | None = None) -> np.ndarray:
+def logits(w: Workload, seed: int = 0, hot_bias: float | None = None,
+           batch: int = 0) -> np.ndarray:
     """Router logits [T, E] fp32: N(0,1) + boost on the token's cluster."""
-    ss = np.random.SeedSequence(seed).spawn(5)
+    ss = _batch_streams(seed, batch)
     rng = np.random.Generator(np.random.PCG64(ss[_S_NOISE]))
     L = rng.standard_normal((w.T, w.E), dtype=np.float32)
     pi = cluster_perm(w, seed)
     s = w.E // w.clusters
     members = pi.reshape(w.clusters, s)                 # [C, s]
-    tc = token_clusters(w, seed)
+    tc = token_clusters(w, seed, batch)
     rows = np.repeat(np.arange(w.T), s)
     cols = members[tc].reshape(-1)
     L[rows, cols] += np.float32(w.boost)
     hb = w.hot_bias if hot_bias is None else hot_bias
     if hb:
         L[:, pi[0]] += np.float32(hb)
+    return L
+
+
+def next_layer_logits(w: Workload, seed: int = 0, follow: float = 0.8,
+                      batch: int = 0) -> np.ndarray:
+    """Router logits [T, E] of the following MoE layer, correlated with this
+    layer's (Zyphra page, English abstract: the experts a token selects at one
+    layer predict those it selects at the next). The next layer has its own
+    latent clusters (a fresh expert permutation); token t's next-layer
+    cluster is sigma(c_t), sigma a seeded permutation of the clusters and c_t
+    its cluster here, with probability ``follow``, else a fresh draw from the
+    same Zipf law. Noise, boost and hot bias as in :func:`logits`; ``batch``
+    as there (same model, other tokens)."""
+    ss = np.random.SeedSequence([seed, 1]).spawn(4)
+    if batch:
+        ss = ss[:1] + np.random.SeedSequence([seed, 1, 1000 + batch]).spawn(3)
+    g = [np.random.Generator(np.random.PCG64(x)) for x in ss]
+    C, s = w.clusters, w.E // w.clusters
+    pi2 = g[0].permutation(w.E).astype(np.int32)
+    sigma = g[0].permutation(C)
+    if w.zipf > 0:
+        p = (np.arange(1, C + 1, dtype=np.float64)) ** (-w.zipf)
+        p /= p.sum()
+    else:
+        p = np.full(C, 1.0 / C)
+    tc = token_clusters(w, seed, batch)
+    fresh = g[1].choice(C, size=w.T, p=p)
+    keep = g[1].random(w.T) < follow
+    tc2 = np.where(keep, sigma[tc], fresh)
+    L = g[2].standard_normal((w.T, w.E), dtype=np.float32)
+    members = pi2.reshape(C, s)
+    rows = np.repeat(np.arange(w.T), s)
+    L[rows, members[tc2].reshape(-1)] += np.float32(w.boost)
+    if w.hot_bias:
+        L[:, pi2[0]] += np.float32(w.hot_bias)
     return L
 
 
