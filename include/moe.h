@@ -163,6 +163,39 @@ moe_status moe_replica_layout(const int32_t* topk_idx, int32_t T, int32_t E, int
                               int32_t* slot_of, void* x_disp, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device workspace moe_token_shuffle needs (host call, no GPU). */
+size_t moe_shuffle_workspace_bytes(int32_t T, int32_t G);
+
+/*
+ * Token shuffling (Zyphra correlated expert placement page, English
+ * abstract: under sequence parallelism each token is moved, during the
+ * reduce-scatter after attention, to the GPU predicted to hold its
+ * next-layer experts). The pages give no prediction rule; here the caller's
+ * affinity table is the prediction model:
+ *  want_idx [T,k] int32: the token's experts the prediction starts from
+ *           (e.g. this layer's routing); entries outside [0,E) add nothing.
+ *  aff      [E,G] int32: aff[e][g] = how strongly a token using expert e is
+ *           expected to need rank g next (e.g. cross-layer co-activation
+ *           counts summed over the next layer's experts on g; the one-hot
+ *           table of a placement gives "the rank holding most of them").
+ * Destination of token t: the rank g maximising sum_j aff[want[t,j]][g]
+ * (int64 sums; ties: the home rank t*G/T, then the lowest rank).
+ * Outputs:
+ *  dest     [T] int32: destination rank of each token.
+ *  rank_off [G+1] int32: token offsets per rank in the shuffled order.
+ *  perm     [T] int32: tokens in shuffled order (grouped by destination,
+ *           ascending within a rank).
+ *  pos      [T] int32: position of token t in that order (perm[pos[t]] = t).
+ *  x_shuf   [T,d] (dt): x[perm[i]] in row i; ignored if x is NULL.
+ *  workspace: device scratch of at least moe_shuffle_workspace_bytes().
+ * G <= 32, k <= 16.
+ */
+moe_status moe_token_shuffle(const int32_t* want_idx, int32_t T, int32_t E, int32_t k,
+                             const int32_t* aff, int32_t G, const void* x, int32_t d,
+                             moe_dtype dt, int32_t* dest, int32_t* rank_off, int32_t* perm,
+                             int32_t* pos, void* x_shuf, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /*
  * Expert networks, first half: for every slot s of expert e (expert_off),
  *   a = x_disp[perm_row[s]],  u = W_gate[e] a,  v = W_up[e] a,

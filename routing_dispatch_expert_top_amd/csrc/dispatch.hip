@@ -328,6 +328,51 @@ __global__ __launch_bounds__(256) void replica_assign_kernel(
   if (t < T && j == 0) node_mask[t] = nm;
 }
 
+// Token shuffling destinations (Zyphra correlated expert placement page,
+// English abstract: under sequence parallelism each token moves, during the
+// reduce-scatter after attention, to the GPU predicted to hold its
+// next-layer experts). Token t goes to the rank g with the largest score
+// sum_j aff[want[t, j]][g] over its valid experts (ties: its home rank
+// t * G / T, then the lowest rank).
+//
+// gfx950 mapping: one lane per (token, rank). A token owns P consecutive
+// lanes (P = power of two >= G), so a wavefront scores 64 / P tokens; each
+// lane gathers its rank's column entry of the token's k table rows (the
+// table is E * G * 4 bytes and stays in cache), the group maximum is an xor
+// butterfly over P lanes, and a ballot of the lanes at the maximum applies
+// the tie rules. Block 0 also writes the identity map rank -> rank that the
+// layout kernels use as the placement of the "experts" 0..G-1.
+__global__ __launch_bounds__(256) void token_dest_kernel(
+    const int32_t* __restrict__ want, int T, int E, int k, const int32_t* __restrict__ aff, int G,
+    int log_p, int32_t* __restrict__ dest, int32_t* __restrict__ ident) {
+  if (blockIdx.x == 0 && threadIdx.x < (unsigned)G) ident[threadIdx.x] = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int P = 1 << log_p;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = (int)(gt >> log_p);
+  const int g = lane & (P - 1);
+  const int base = lane & ~(P - 1);
+  int64_t sc = INT64_MIN;
+  if (t < T && g < G) {
+    sc = 0;
+    for (int j = 0; j < k; ++j) {
+      const int e = want[(size_t)t * k + j];
+      if (e >= 0 && e < E) sc += aff[(size_t)e * G + g];
+    }
+  }
+  int64_t mx = sc;
+  for (int off = 1; off < P; off <<= 1) {
+    const int64_t o = __shfl_xor((long long)mx, off, kWave);
+    mx = o > mx ? o : mx;
+  }
+  const uint64_t grp = (P == kWave ? ~0ull : ((1ull << P) - 1ull)) << base;
+  const uint64_t top = __ballot(t < T && g < G && sc == mx) & grp;
+  if (t < T && g == 0) {
+    const int home = (int)((int64_t)t * G / T);
+    dest[t] = ((top >> (base + home)) & 1ull) ? home : __ffsll((unsigned long long)top) - 1 - base;
+  }
+}
+
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -439,4 +484,63 @@ MOE_EXPORT moe_status moe_replica_layout(const int32_t* topk_idx, int32_t T, int
   return layout_impl(topk_idx, T, E, k, nullptr, rank_of, G, x, d, dt, rank_mask, rank_off,
                      disp_token, expert_off, perm_row, slot_of, x_disp, workspace,
                      workspace_bytes, stream);
+}
+
+namespace moe {
+namespace {
+
+struct ShuffleWorkspace {
+  size_t ident, rank_mask, expert_off, perm_row, layout, total;
+};
+inline ShuffleWorkspace shuffle_workspace(int32_t T, int32_t G) {
+  ShuffleWorkspace w;
+  w.ident = 0;
+  w.rank_mask = w.ident + align_up((size_t)G * sizeof(int32_t));
+  w.expert_off = w.rank_mask + align_up((size_t)T * sizeof(uint32_t));
+  w.perm_row = w.expert_off + align_up((size_t)(G + 1) * sizeof(int32_t));
+  w.layout = w.perm_row + align_up((size_t)T * sizeof(int32_t));
+  w.total = w.layout + workspace_layout(T, G, 1, G).total;
+  return w;
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_EXPORT size_t moe_shuffle_workspace_bytes(int32_t T, int32_t G) {
+  if (T < 0 || G < 1 || G > kMaxG) return 0;
+  return shuffle_workspace(T, G).total;
+}
+
+MOE_EXPORT moe_status moe_token_shuffle(const int32_t* want_idx, int32_t T, int32_t E, int32_t k,
+                                        const int32_t* aff, int32_t G, const void* x, int32_t d,
+                                        moe_dtype dt, int32_t* dest, int32_t* rank_off,
+                                        int32_t* perm, int32_t* pos, void* x_shuf,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || G < 1) return MOE_ERR_ARG;
+  if (k > kMaxK || G > kMaxG || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!aff || !rank_off || (T > 0 && (!want_idx || !dest || !perm || !pos))) return MOE_ERR_ARG;
+  if (x) {  // checked here so that nothing is enqueued on an argument error
+    if (!valid_dtype(dt) || d < 1 || (T > 0 && !x_shuf)) return MOE_ERR_ARG;
+    if (((size_t)d * dtype_bytes(dt)) % 16 != 0 || (uintptr_t)x % 16 || (uintptr_t)x_shuf % 16)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  const ShuffleWorkspace ws = shuffle_workspace(T, G);
+  if (!workspace || workspace_bytes < ws.total) return MOE_ERR_WORKSPACE;
+  char* wsp = static_cast<char*>(workspace);
+  int32_t* ident = reinterpret_cast<int32_t*>(wsp + ws.ident);
+  int log_p = 0;
+  while ((1 << log_p) < G) ++log_p;  // G <= 32: a token's lanes fit in a wave
+  const int64_t lanes = (int64_t)(T > 0 ? T : 1) << log_p;
+  hipLaunchKernelGGL(token_dest_kernel, dim3((unsigned)ceil_div(lanes, 256)), dim3(256), 0, stream,
+                     want_idx, T, E, k, aff, G, log_p, dest, ident);
+  // The shuffled order is the once-per-rank layout of a batch in which token
+  // t has the single choice dest[t] and "expert" g sits on rank g: its rows
+  // are the tokens grouped by rank (perm), its slots give each token's
+  // position in that order (pos), and its dispatched rows are x[perm].
+  return layout_impl(dest, T, G, 1, ident, nullptr, G, x, d, dt,
+                     reinterpret_cast<uint32_t*>(wsp + ws.rank_mask), rank_off, perm,
+                     reinterpret_cast<int32_t*>(wsp + ws.expert_off),
+                     reinterpret_cast<int32_t*>(wsp + ws.perm_row), pos, x_shuf, wsp + ws.layout,
+                     workspace_bytes - ws.layout, stream);
 }

@@ -54,6 +54,9 @@ def lib():
                                           p, p, p]),
             "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
             "moe_plan_placement": (C.c_int, [p, p, i32, i32, i32, i32, p]),
+            "moe_shuffle_workspace_bytes": (sz, [i32, i32]),
+            "moe_token_shuffle": (C.c_int, [p, i32, i32, i32, p, i32, p, i32, C.c_int, p, p, p,
+                                            p, p, p, sz, p]),
             "moe_replica_layout": (C.c_int, [p, i32, i32, i32, p, i32, i32, p, i32, C.c_int,
                                              p, p, p, p, p, p, p, p, p, p, sz, p]),
         }
@@ -186,6 +189,30 @@ def moe_replica_layout(topk_idx, E, rep_mask, G, ranks_per_node, x=None, out=Non
         _ptr(out["rank_mask"]), _ptr(out["rank_off"]), _ptr(out["disp_token"]),
         _ptr(out["expert_off"]), _ptr(out["perm_row"]), _ptr(out["slot_of"]),
         _ptr(out.get("x_disp")) if x is not None else None, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def moe_token_shuffle(want_idx, aff, x=None, out=None, stream=None):
+    """want_idx [T,k] int32, aff [E,G] int32 device tensors. Returns a dict
+    with dest, rank_off, perm, pos (and x_shuf if x is given)."""
+    T, k = want_idx.shape
+    E, G = aff.shape
+    dev = want_idx.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(dest=torch.empty(T, **i32), rank_off=torch.empty(G + 1, **i32),
+                   perm=torch.empty(T, **i32), pos=torch.empty(T, **i32),
+                   workspace=torch.empty(max(1, int(lib().moe_shuffle_workspace_bytes(T, G))),
+                                         dtype=torch.uint8, device=dev))
+        if x is not None:
+            out["x_shuf"] = torch.empty_like(x)
+    dt = dtype_code(x) if x is not None else MOE_F32
+    ws = out["workspace"]
+    _check("moe_token_shuffle", lib().moe_token_shuffle(
+        _ptr(want_idx), T, E, k, _ptr(aff), G, _ptr(x), x.shape[1] if x is not None else 0, dt,
+        _ptr(out["dest"]), _ptr(out["rank_off"]), _ptr(out["perm"]), _ptr(out["pos"]),
+        _ptr(out.get("x_shuf")) if x is not None else None, _ptr(ws), ws.numel(),
         _stream(stream)))
     return out
 
