@@ -228,11 +228,67 @@ moe_status moe_grouped_ffn(const void* x_disp, const int32_t* perm_row, const in
  * Combine back to token order (Zyphra page, English abstract: the expert
  * results are combined): out[t] = sum_j gates[t,j] * y[slot_of[t*k+j]],
  * accumulated in fp32 in j order, stored in dt (bf16: RNE).
- *  y [T*k,d] (dt), slot_of [T*k], gates [T,k] fp32, out [T,d] (dt) out.
+ *  y [T*k,d] (dt), slot_of [T*k], gates [T,k] fp32 (NULL: every gate is
+ *  1), out [T,d] (dt) out.
  */
 moe_status moe_combine(const void* y, const int32_t* slot_of, const float* gates,
                        int32_t T, int32_t k, int32_t d, moe_dtype dt, void* out,
                        hipStream_t stream);
+
+/*
+ * ---- Backward pass (training). The pages train these layers: expert
+ * parallelism runs its all-to-all in the forward and the backward pass
+ * (Zyphra correlated expert placement page, English abstract). Each call is
+ * the exact gradient of the matching forward step for a loss whose gradient
+ * at the layer output is dout; weight gradients are written (not added) in
+ * fp32, activation gradients in dt. Slots, offsets and permutations are
+ * those of the forward's layout.
+ */
+
+/* Forward gate/up that also keeps the pre-activations for the backward:
+ * uv [T*k, 2F] (dt): row s = [u_s | v_s] (u = W_gate a, v = W_up a). */
+moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t* perm_row,
+                                   const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
+                                   int32_t d, int32_t F, const void* w_gate, const void* w_up,
+                                   moe_dtype dt, void* h, void* uv, hipStream_t stream);
+
+/* Combine backward: dy[slot_of[t*k+j]] = gates[t,j] * dout[t] (dt) and
+ * dgates[t,j] = <dout[t], y[slot_of[t*k+j]]> (fp32 accumulation).
+ *  dout [T,d], y [T*k,d], dy [T*k,d] (dt); gates, dgates [T,k] fp32. */
+moe_status moe_combine_bwd(const void* dout, const void* y, const int32_t* slot_of,
+                           const float* gates, int32_t T, int32_t k, int32_t d, moe_dtype dt,
+                           void* dy, float* dgates, hipStream_t stream);
+
+/* Down projection and SwiGLU backward, per expert e over its slots s:
+ *  dh = dy[s] W_down[e];  du = dh * v * silu'(u),  dv = dh * silu(u)
+ *  (silu'(u) = sg (1 + u (1 - sg)), sg = 1 / (1 + e^-u); u, v from uv);
+ *  duv [T*k, 2F] (dt) out: row s = [du_s | dv_s];
+ *  dw_down [E,d,F] fp32 out: dw_down[e] = sum_s dy[s] h[s]^T (zero for an
+ *  expert without slots). h [T*k,F], uv [T*k,2F], w_down [E,d,F] (dt). */
+moe_status moe_expert_down_bwd(const void* dy, const void* h, const void* uv,
+                               const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
+                               int32_t d, int32_t F, const void* w_down, moe_dtype dt, void* duv,
+                               float* dw_down, hipStream_t stream);
+
+/* Gate/up backward, per expert e over its slots s (a_s = x_disp[perm_row[s]]):
+ *  da [T*k,d] (dt) out: da[s] = du_s W_gate[e] + dv_s W_up[e];
+ *  dw_gate, dw_up [E,F,d] fp32 out: sum_s du_s a_s^T and sum_s dv_s a_s^T. */
+moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp, const int32_t* perm_row,
+                                  const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
+                                  int32_t d, int32_t F, const void* w_gate, const void* w_up,
+                                  moe_dtype dt, void* da, float* dw_gate, float* dw_up,
+                                  hipStream_t stream);
+
+/* Dispatch backward: dx[t] = sum_j da[slot_of[t*k+j]] (fp32 accumulation in
+ * j order, stored in dt). da [T*k,d], dx [T,d]. */
+moe_status moe_dispatch_bwd(const void* da, const int32_t* slot_of, int32_t T, int32_t k,
+                            int32_t d, moe_dtype dt, void* dx, hipStream_t stream);
+
+/* Routing backward (softmax over the chosen logits):
+ *  dlogits[t, topk_idx[t,j]] = g_j (dg_j - sum_i g_i dg_i), every other
+ *  entry 0. gates, dgates [T,k] fp32, dlogits [T,E] fp32 out. E <= 1024. */
+moe_status moe_route_bwd(const float* gates, const float* dgates, const int32_t* topk_idx,
+                         int32_t T, int32_t E, int32_t k, float* dlogits, hipStream_t stream);
 
 /*
  * Expert placement planner (host code; every pointer is HOST memory).

@@ -1,0 +1,667 @@
+// Backward pass of the MoE layer: the exact gradient of the forward for a
+// loss whose gradient at the layer output is dout.
+//
+// The pages train these layers: expert parallelism runs its all-to-all in
+// the forward and the backward pass (Zyphra correlated expert placement
+// page, English abstract). The backward steps, in order:
+//   combine   dy[slot(t,j)] = g_tj dout[t],  dgates[t,j] = <dout[t], y_tj>
+//   down      dh = dy W_down[e] (then SwiGLU backward with the saved u, v:
+//             du = dh v silu'(u), dv = dh silu(u)),  dW_down[e] = dy^T h
+//   gate/up   da = du W_gate[e] + dv W_up[e],  dW_gate[e] = du^T a,
+//             dW_up[e] = dv^T a
+//   dispatch  dx[t] = sum_j da[slot(t,j)]
+//   routing   dlogits[t, idx[t,j]] = g_j (dg_j - sum_i g_i dg_i), else 0
+//
+// gfx950 mapping of the two GEMM shapes:
+//   data gradients: rows = an expert's slots (ragged), the weight panel is
+//     read with its output dimension contiguous ([K][N] rows);
+//   weight gradients: the reduction runs over an expert's slots (ragged K),
+//     both operands have their output dimension contiguous.
+// Both use one register-staged MFMA kernel: each thread fetches 8 rows x 16
+// bytes of an operand whose K index is the row, transposes that 8 x 8 bf16
+// block in registers (byte permutes), and writes 8 K-contiguous 16-byte
+// chunks into LDS; operands that are already K-contiguous go straight in.
+// The LDS image and the fragment reads are those of the forward kernel
+// (XOR-swizzled 16-byte chunks), the MFMA is v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation, and the next K slice is fetched into registers while
+// the current one is multiplied.
+#include "moe_internal.h"
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------- combine backward
+
+// One wavefront per token: dout[t] is read once; for each choice the lane
+// chunk of y's row feeds the dot product (fp32) and the scaled dout chunk is
+// written to dy's row. dgates comes out of a wave reduction per choice.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const u32x4* __restrict__ dout, const u32x4* __restrict__ y,
+    const int32_t* __restrict__ slot_of, const float* __restrict__ gates, int T, int k,
+    int row_vecs, u32x4* __restrict__ dy, float* __restrict__ dgates) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * (blockDim.x / kWave) + wave;
+  if (t >= T) return;
+  float dot[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) dot[j] = 0.f;
+  const u32x4* o = dout + (size_t)t * row_vecs;
+  for (int c = lane; c < row_vecs; c += kWave) {
+    const u32x4 ov = __builtin_nontemporal_load(o + c);
+    float of[8];
+    if (BF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        of[2 * q] = bf16lo(ov[q]);
+        of[2 * q + 1] = bf16hi(ov[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) of[q] = __uint_as_float(ov[q]);
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) continue;
+      const int s = slot_of[(size_t)t * k + j];
+      const float g = gates[(size_t)t * k + j];
+      const u32x4 yv = __builtin_nontemporal_load(y + (size_t)s * row_vecs + c);
+      u32x4 w;
+      if (BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          dot[j] = fmaf(of[2 * q], bf16lo(yv[q]), dot[j]);
+          dot[j] = fmaf(of[2 * q + 1], bf16hi(yv[q]), dot[j]);
+          w[q] = pack_bf16x2(g * of[2 * q], g * of[2 * q + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          dot[j] = fmaf(of[q], __uint_as_float(yv[q]), dot[j]);
+          w[q] = __float_as_uint(g * of[q]);
+        }
+      }
+      dy[(size_t)s * row_vecs + c] = w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) continue;
+    float v = dot[j];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (lane == 0) dgates[(size_t)t * k + j] = v;
+  }
+}
+
+// ---------------------------------------------------------------- routing backward
+
+// One wavefront per token: lanes j < k hold the gates and their gradients;
+// the inner product sum_i g_i dg_i is a wave sum; every lane then writes its
+// share of the token's E logit gradients (0 for experts not chosen).
+__global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict__ gates,
+                                                        const float* __restrict__ dgates,
+                                                        const int32_t* __restrict__ topk_idx,
+                                                        int T, int E, int k,
+                                                        float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * (blockDim.x / kWave) + wave;
+  if (t >= T) return;
+  float g = 0.f, dg = 0.f;
+  int e = -1;
+  if (lane < k) {
+    g = gates[(size_t)t * k + lane];
+    dg = dgates[(size_t)t * k + lane];
+    e = topk_idx[(size_t)t * k + lane];
+  }
+  float inner = g * dg;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) inner += __shfl_xor(inner, off, kWave);
+  const float mine = g * (dg - inner);
+  // every lane gets the k (expert, gradient) pairs while all lanes are active
+  int ej[kMaxK];
+  float vj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    ej[j] = __shfl(e, j, kWave);
+    vj[j] = __shfl(mine, j, kWave);
+  }
+  for (int c = lane; c < E; c += kWave) {
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k && ej[j] == c) v = vj[j];
+    dlogits[(size_t)t * E + c] = v;
+  }
+}
+
+// ---------------------------------------------------------------- GEMM descriptors
+
+enum BwdMode : int {
+  kDgradSwiglu = 0,  // dh = dy W_down[e]; epilogue: SwiGLU backward -> du, dv
+  kDgradPlain = 1,   // da = [du dv] [W_gate[e]; W_up[e]]
+  kWgrad = 2,        // dW[e] = A_e^T B_e over the expert's slots
+};
+
+struct BwdArgs {
+  const int32_t* expert_off;
+  int E;
+  // data gradients: C[s][n] = sum_k A[s][k] W[e][k][n], k < ksplit from W0
+  // (row k), else from W1 (row k - ksplit); W panels are K x N0, estride
+  // elements apart
+  const uint16_t* A;
+  int lda, K, N0, ksplit;
+  const uint16_t* W0;
+  const uint16_t* W1;
+  size_t estride;
+  uint16_t* C;     // plain: [S][ldc]
+  int ldc;
+  const uint16_t* uv;  // swiglu: saved [S][2F] (u then v), output duv [S][2F]
+  uint16_t* duv;
+  int F;
+  // weight gradients: Out[e][m][n] = sum_s At[s][m] Bt[row(s)][n], rows m <
+  // msplit to O0 (msplit x N0 per expert), the others to O1; row(s) =
+  // b_gather[s] if given
+  const uint16_t* At;
+  int ldat, M0;
+  const uint16_t* Bt;
+  const int32_t* b_gather;
+  int ldbt, msplit;
+  float* O0;
+  float* O1;
+};
+
+// 8 x 8 transpose of bf16: r[i] holds 8 values of K row i (8 consecutive
+// M/N indices); o[c] gets the 8 K values of index c ^ flip (flip = 0 or 1,
+// per lane). Word q of o[c] packs K rows 2q (low half) and 2q+1 (high
+// half); v_perm_b32 picks the half of the index from each (byte selector
+// 0x05040100: both low halves, 0x07060302: both high halves). Indices c and
+// c ^ 1 share their source words, so flipping only swaps the two selectors.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8], bool flip) {
+  const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? sel_odd : sel_even;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[c][q] = __builtin_amdgcn_perm(r[2 * q + 1][c >> 1], r[2 * q][c >> 1], sel);
+  }
+}
+
+__device__ __forceinline__ void silu_parts(float u, float& silu, float& dsilu) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * 1.44269504088896341f));
+  silu = u * sg;
+  dsilu = sg * (1.0f + u * (1.0f - sg));
+}
+
+// ---------------------------------------------------------------- bf16 MFMA GEMM
+
+constexpr int kBBM = 256, kBBN = 256, kBBK = 64;  // tile; 4 waves as 2 x 2 of 128 x 128
+constexpr int kBCH = kBBK / 8;                     // 16-byte chunks per LDS row
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_bwd_bf16_kernel(BwdArgs p) {
+  constexpr int BM = kBBM, BN = kBBN, BK = kBBK, CH = kBCH;
+  constexpr int TM = 4, TN = 4;
+  __shared__ u32x4 lds[2][(BM + BN) * CH];  // 128 KiB: two stages of A then B rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+  // ---- tile
+  int e, mt, nt, seg0, seg1, m0, c0, KT;
+  if (MODE != kWgrad) {
+    Sched& sc = *reinterpret_cast<Sched*>(&lds[0][0]);
+    build_schedule(sc, p.expert_off, p.E, BM);
+    const int NT = (p.N0 + BN - 1) / BN;
+    const int tile = xcd_logical_tile(sc.mt_off[p.E] * NT);
+    if (tile < 0) return;
+    decode_tile(sc, p.E, NT, tile, e, nt, mt);
+    __syncthreads();
+    seg0 = p.expert_off[e];
+    seg1 = p.expert_off[e + 1];
+    m0 = seg0 + mt * BM;
+    c0 = nt * BN;
+    KT = p.K / BK;
+  } else {
+    const int MT = (p.M0 + BM - 1) / BM, NT = (p.N0 + BN - 1) / BN;
+    const int tile = xcd_logical_tile(p.E * MT * NT);
+    if (tile < 0) return;
+    e = tile / (MT * NT);
+    const int rem = tile - e * MT * NT;
+    mt = rem / NT;
+    nt = rem % NT;
+    seg0 = p.expert_off[e];
+    seg1 = p.expert_off[e + 1];
+    m0 = mt * BM;
+    c0 = nt * BN;
+    KT = (seg1 - seg0 + BK - 1) / BK;
+  }
+
+  // ---- global -> registers
+  // K-contiguous operand (data-gradient A): thread -> chunk tid % 8 of rows
+  // tid / 8 + 32 i. Row-major operands with K as the row: thread -> 8 x 8
+  // block (K group kg = tid % 8, index chunk nc = tid / 8).
+  const int kg = tid & 7, nc = tid >> 3;
+  u32x4 ra[8], rb[8];
+  auto load = [&](int kt) {
+    const int k0 = kt * BK;
+    if (MODE != kWgrad) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = nc + 32 * i;
+        const int s = min(m0 + r, seg1 - 1);
+        ra[i] = *reinterpret_cast<const u32x4*>(p.A + (size_t)s * p.lda + k0 + kg * 8);
+      }
+      const bool hi = k0 >= p.ksplit;  // uniform over the slice (ksplit % BK == 0)
+      const uint16_t* w = (hi ? p.W1 : p.W0) + (size_t)e * p.estride;
+      const int kr = (hi ? k0 - p.ksplit : k0) + kg * 8;
+      const int n = min(c0 + nc * 8, p.N0 - 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rb[i] = *reinterpret_cast<const u32x4*>(w + (size_t)(kr + i) * p.N0 + n);
+    } else {
+      // Rows past the expert's last slot read its last slot (in bounds) and
+      // their A values are zeroed: zero times a finite B value adds nothing.
+      // All gather indices are fetched first and then all 16 data loads, so a
+      // slice costs two memory round trips, not one per row.
+      const int m = min(m0 + nc * 8, p.M0 - 8);
+      const int n = min(c0 + nc * 8, p.N0 - 8);
+      int srow[8], brow[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) srow[i] = min(seg0 + k0 + kg * 8 + i, seg1 - 1);
+      if (p.b_gather) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) brow[i] = p.b_gather[srow[i]];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) brow[i] = srow[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ra[i] = *reinterpret_cast<const u32x4*>(p.At + (size_t)srow[i] * p.ldat + m);
+        rb[i] = *reinterpret_cast<const u32x4*>(p.Bt + (size_t)brow[i] * p.ldbt + n);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (seg0 + k0 + kg * 8 + i >= seg1) ra[i] = u32x4{0, 0, 0, 0};
+    }
+  };
+  // registers -> LDS stage. Transposed blocks: at store c a lane writes row
+  // nc * 8 + (c ^ (nc & 1)), so the 16 lanes of one LDS pass cover rows of
+  // both parities (all 16 bank groups of 256 bytes).
+  const int odd = nc & 1;
+  auto store_t = [&](u32x4* base, const u32x4 (&r)[8]) {
+    u32x4 o[8];
+    transpose8x8(r, o, odd);  // o[c] = index c ^ odd
+#pragma unroll
+    for (int c = 0; c < 8; ++c) base[swz_ch<CH>(nc * 8 + (c ^ odd), kg)] = o[c];
+  };
+  auto store = [&](int st) {
+    u32x4* As = lds[st];
+    u32x4* Bs = lds[st] + BM * CH;
+    if (MODE != kWgrad) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) As[swz_ch<CH>(nc + 32 * i, kg)] = ra[i];
+    } else {
+      store_t(As, ra);
+    }
+    store_t(Bs, rb);
+  };
+
+  // ---- MFMA fragments: wave (wm, wn) owns rows wm*128.. of A, wn*128.. of B
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, lk = lane >> 5;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (KT > 0) load(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+    store(st);
+    __syncthreads();
+    if (kt + 1 < KT) load(kt + 1);
+    const u32x4* As = lds[st];
+    const u32x4* Bs = lds[st] + BM * CH;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = ks * 2 + lk;
+      bf16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        fa[tm] = __builtin_bit_cast(bf16x8, As[swz_ch<CH>(wm * 128 + tm * 32 + li, ch)]);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        fb[tn] = __builtin_bit_cast(bf16x8, Bs[swz_ch<CH>(wn * 128 + tn * 32 + li, ch)]);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          // B fragment first: lane holds 4 consecutive output columns of one row
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane owns row (.. + li) and, per register quad qd, output
+  // columns 8 qd + 4 lk + 0..3 of each 32-wide column tile
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int row = m0 + wm * 128 + tm * 32 + li;
+    if (MODE != kWgrad ? row >= seg1 : row >= p.M0) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int col = c0 + wn * 128 + tn * 32 + 8 * qd + 4 * lk;
+        if (col >= p.N0) continue;
+        const f32x16& a = acc[tm][tn];
+        if (MODE == kDgradPlain) {
+          uint2 pk;
+          pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
+          pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
+          *reinterpret_cast<uint2*>(p.C + (size_t)row * p.ldc + col) = pk;
+        } else if (MODE == kDgradSwiglu) {
+          const size_t o = (size_t)row * (2 * p.F) + col;
+          const uint2 uu = *reinterpret_cast<const uint2*>(p.uv + o);
+          const uint2 vv = *reinterpret_cast<const uint2*>(p.uv + o + p.F);
+          const float u[4] = {bf16lo(uu.x), bf16hi(uu.x), bf16lo(uu.y), bf16hi(uu.y)};
+          const float v[4] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y)};
+          float du[4], dv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float sl, ds;
+            silu_parts(u[i], sl, ds);
+            du[i] = a[4 * qd + i] * v[i] * ds;
+            dv[i] = a[4 * qd + i] * sl;
+          }
+          uint2 pu, pv;
+          pu.x = pack_bf16x2(du[0], du[1]);
+          pu.y = pack_bf16x2(du[2], du[3]);
+          pv.x = pack_bf16x2(dv[0], dv[1]);
+          pv.y = pack_bf16x2(dv[2], dv[3]);
+          *reinterpret_cast<uint2*>(p.duv + o) = pu;
+          *reinterpret_cast<uint2*>(p.duv + o + p.F) = pv;
+        } else {
+          float* out = row < p.msplit
+                           ? p.O0 + ((size_t)e * p.msplit + row) * p.N0
+                           : p.O1 + ((size_t)e * (p.M0 - p.msplit) + (row - p.msplit)) * p.N0;
+          *reinterpret_cast<f32x4*>(out + col) =
+              f32x4{a[4 * qd + 0], a[4 * qd + 1], a[4 * qd + 2], a[4 * qd + 3]};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 SIMT GEMM
+
+// The same three GEMMs in fp32 with plain FMA (64 x 64 tiles, 16-deep K
+// slices, element loads through the mode's index map).
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(BwdArgs p, const float* A,
+                                                           const float* W0, const float* W1,
+                                                           float* C, const float* uv, float* duv,
+                                                           const float* At, const float* Bt) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  __shared__ Sched sc;
+  int e, mt, nt, seg0, seg1, m0, c0, Kt;
+  if (MODE != kWgrad) {
+    build_schedule(sc, p.expert_off, p.E, BM);
+    const int NT = (p.N0 + BN - 1) / BN;
+    const int tile = xcd_logical_tile(sc.mt_off[p.E] * NT);
+    if (tile < 0) return;
+    decode_tile(sc, p.E, NT, tile, e, nt, mt);
+    seg0 = p.expert_off[e];
+    seg1 = p.expert_off[e + 1];
+    m0 = seg0 + mt * BM;
+    c0 = nt * BN;
+    Kt = p.K;
+  } else {
+    const int MT = (p.M0 + BM - 1) / BM, NT = (p.N0 + BN - 1) / BN;
+    const int tile = xcd_logical_tile(p.E * MT * NT);
+    if (tile < 0) return;
+    e = tile / (MT * NT);
+    const int rem = tile - e * MT * NT;
+    mt = rem / NT;
+    nt = rem % NT;
+    seg0 = p.expert_off[e];
+    seg1 = p.expert_off[e + 1];
+    m0 = mt * BM;
+    c0 = nt * BN;
+    Kt = seg1 - seg0;
+  }
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < Kt; k0 += BK) {
+    for (int q = tid; q < BK * BM; q += 256) {
+      const int kk = q / BM, r = q % BM, k = k0 + kk;
+      float av = 0.f, bv = 0.f;
+      if (MODE != kWgrad) {
+        const int s = min(m0 + r, seg1 - 1);
+        av = A[(size_t)s * p.lda + k];
+        const int n = min(c0 + r, p.N0 - 1);
+        const float* w = k < p.ksplit ? W0 + (size_t)e * p.estride + (size_t)k * p.N0
+                                      : W1 + (size_t)e * p.estride + (size_t)(k - p.ksplit) * p.N0;
+        bv = w[n];
+      } else if (k < Kt) {
+        const int s = seg0 + k;
+        const int m = min(m0 + r, p.M0 - 1), n = min(c0 + r, p.N0 - 1);
+        av = At[(size_t)s * p.ldat + m];
+        bv = Bt[(size_t)(p.b_gather ? p.b_gather[s] : s) * p.ldbt + n];
+      }
+      As[kk][r] = av;
+      Bs[kk][r] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(As[kk][ty * 4 + i], Bs[kk][tx * 4 + j], acc[i][j]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (MODE != kWgrad ? row >= seg1 : row >= p.M0) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = c0 + tx * 4 + j;
+      if (col >= p.N0) continue;
+      if (MODE == kDgradPlain) {
+        C[(size_t)row * p.ldc + col] = acc[i][j];
+      } else if (MODE == kDgradSwiglu) {
+        const size_t o = (size_t)row * (2 * p.F) + col;
+        const float u = uv[o], v = uv[o + p.F];
+        float sl, ds;
+        silu_parts(u, sl, ds);
+        duv[o] = acc[i][j] * v * ds;
+        duv[o + p.F] = acc[i][j] * sl;
+      } else {
+        float* out = row < p.msplit
+                         ? p.O0 + ((size_t)e * p.msplit + row) * p.N0
+                         : p.O1 + ((size_t)e * (p.M0 - p.msplit) + (row - p.msplit)) * p.N0;
+        out[col] = acc[i][j];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int MODE>
+void launch_gemm_bwd(const BwdArgs& p, moe_dtype dt, int64_t rows, hipStream_t stream) {
+  int64_t tiles;
+  if (dt == MOE_BF16) {
+    tiles = MODE == kWgrad ? (int64_t)p.E * ceil_div(p.M0, kBBM) * ceil_div(p.N0, kBBN)
+                           : mtile_upper(rows, p.E, kBBM) * ceil_div(p.N0, kBBN);
+    hipLaunchKernelGGL(gemm_bwd_bf16_kernel<MODE>, dim3(grid_for(tiles)), dim3(256), 0, stream, p);
+  } else {
+    tiles = MODE == kWgrad ? (int64_t)p.E * ceil_div(p.M0, 64) * ceil_div(p.N0, 64)
+                           : mtile_upper(rows, p.E, 64) * ceil_div(p.N0, 64);
+    hipLaunchKernelGGL(gemm_bwd_f32_kernel<MODE>, dim3(grid_for(tiles)), dim3(256), 0, stream, p,
+                       reinterpret_cast<const float*>(p.A), reinterpret_cast<const float*>(p.W0),
+                       reinterpret_cast<const float*>(p.W1), reinterpret_cast<float*>(p.C),
+                       reinterpret_cast<const float*>(p.uv), reinterpret_cast<float*>(p.duv),
+                       reinterpret_cast<const float*>(p.At), reinterpret_cast<const float*>(p.Bt));
+  }
+}
+
+moe_status check_bwd(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
+  if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || F < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK || (int64_t)T * k >= (1ll << 31) || d % 64 || F % 64)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if ((uintptr_t)q % 16) return true;
+  return false;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+MOE_EXPORT moe_status moe_combine_bwd(const void* dout, const void* y, const int32_t* slot_of,
+                                      const float* gates, int32_t T, int32_t k, int32_t d,
+                                      moe_dtype dt, void* dy, float* dgates, hipStream_t stream) {
+  if (T < 0 || k < 1 || d < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
+  if (k > kMaxK || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!dout || !y || !slot_of || !gates || !dy || !dgates) return MOE_ERR_ARG;
+  if (((size_t)d * dtype_bytes(dt)) % 16 || misaligned({dout, y, dy})) return MOE_ERR_UNSUPPORTED;
+  const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);
+  const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
+  if (dt == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<true>, grid, block, 0, stream,
+                       static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
+                       gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<false>, grid, block, 0, stream,
+                       static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
+                       gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
+  return launch_status();
+}
+
+MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const void* uv,
+                                          const int32_t* expert_off, int32_t T, int32_t E,
+                                          int32_t k, int32_t d, int32_t F, const void* w_down,
+                                          moe_dtype dt, void* duv, float* dw_down,
+                                          hipStream_t stream) {
+  moe_status st = check_bwd(T, E, k, d, F, dt);
+  if (st != MOE_OK) return st;
+  if (!expert_off || !w_down || !dw_down || (T > 0 && (!dy || !h || !uv || !duv)))
+    return MOE_ERR_ARG;
+  if (misaligned({dy, h, uv, w_down, duv, dw_down})) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)T * k;
+  BwdArgs p = {};
+  p.expert_off = expert_off;
+  p.E = E;
+  // dh = dy W_down[e]: W_down[e] is d x F = K x N0
+  p.A = static_cast<const uint16_t*>(dy);
+  p.lda = d;
+  p.K = d;
+  p.N0 = F;
+  p.ksplit = d;
+  p.W0 = p.W1 = static_cast<const uint16_t*>(w_down);
+  p.estride = (size_t)d * F;
+  p.uv = static_cast<const uint16_t*>(uv);
+  p.duv = static_cast<uint16_t*>(duv);
+  p.F = F;
+  if (rows > 0) launch_gemm_bwd<kDgradSwiglu>(p, dt, rows, stream);
+  // dW_down[e] = dy^T h: M0 = d, N0 = F, reduction over the expert's slots
+  BwdArgs q = {};
+  q.expert_off = expert_off;
+  q.E = E;
+  q.At = static_cast<const uint16_t*>(dy);
+  q.ldat = d;
+  q.M0 = d;
+  q.Bt = static_cast<const uint16_t*>(h);
+  q.ldbt = F;
+  q.N0 = F;
+  q.msplit = d;
+  q.O0 = q.O1 = dw_down;
+  launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
+  return launch_status();
+}
+
+MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp,
+                                             const int32_t* perm_row, const int32_t* expert_off,
+                                             int32_t T, int32_t E, int32_t k, int32_t d,
+                                             int32_t F, const void* w_gate, const void* w_up,
+                                             moe_dtype dt, void* da, float* dw_gate,
+                                             float* dw_up, hipStream_t stream) {
+  moe_status st = check_bwd(T, E, k, d, F, dt);
+  if (st != MOE_OK) return st;
+  if (!expert_off || !w_gate || !w_up || !dw_gate || !dw_up ||
+      (T > 0 && (!duv || !x_disp || !perm_row || !da)))
+    return MOE_ERR_ARG;
+  if (misaligned({duv, x_disp, w_gate, w_up, da, dw_gate, dw_up})) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)T * k;
+  BwdArgs p = {};
+  p.expert_off = expert_off;
+  p.E = E;
+  // da = du W_gate[e] + dv W_up[e]: K = 2F (rows of W_gate[e], then of W_up[e]), N0 = d
+  p.A = static_cast<const uint16_t*>(duv);
+  p.lda = 2 * F;
+  p.K = 2 * F;
+  p.N0 = d;
+  p.ksplit = F;
+  p.W0 = static_cast<const uint16_t*>(w_gate);
+  p.W1 = static_cast<const uint16_t*>(w_up);
+  p.estride = (size_t)F * d;
+  p.C = static_cast<uint16_t*>(da);
+  p.ldc = d;
+  if (rows > 0) launch_gemm_bwd<kDgradPlain>(p, dt, rows, stream);
+  // [dW_gate; dW_up][e] = [du dv]^T a, a = x_disp[perm_row[s]]: M0 = 2F, N0 = d
+  BwdArgs q = {};
+  q.expert_off = expert_off;
+  q.E = E;
+  q.At = static_cast<const uint16_t*>(duv);
+  q.ldat = 2 * F;
+  q.M0 = 2 * F;
+  q.Bt = static_cast<const uint16_t*>(x_disp);
+  q.b_gather = perm_row;
+  q.ldbt = d;
+  q.N0 = d;
+  q.msplit = F;
+  q.O0 = dw_gate;
+  q.O1 = dw_up;
+  launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
+  return launch_status();
+}
+
+MOE_EXPORT moe_status moe_dispatch_bwd(const void* da, const int32_t* slot_of, int32_t T,
+                                       int32_t k, int32_t d, moe_dtype dt, void* dx,
+                                       hipStream_t stream) {
+  // dx[t] = sum_j da[slot(t, j)]: the combine with every gate equal to one
+  return moe_combine(da, slot_of, nullptr, T, k, d, dt, dx, stream);
+}
+
+MOE_EXPORT moe_status moe_route_bwd(const float* gates, const float* dgates,
+                                    const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                    float* dlogits, hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_ARG;
+  if (k > kMaxK || E > 1024 || (int64_t)T * E >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!gates || !dgates || !topk_idx || !dlogits) return MOE_ERR_ARG;
+  hipLaunchKernelGGL(route_bwd_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, stream,
+                     gates, dgates, topk_idx, T, E, k, dlogits);
+  return launch_status();
+}

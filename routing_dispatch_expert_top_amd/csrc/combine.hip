@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   for (int j = 0; j < KM; ++j) {
     if (j < k) {
       rows[j] = y + (size_t)slot_of[(size_t)t * k + j] * row_vecs;
-      g[j] = gates[(size_t)t * k + j];
+      g[j] = gates ? gates[(size_t)t * k + j] : 1.0f;
     }
   }
   u32x4* o = out + (size_t)t * row_vecs;
@@ -139,7 +139,7 @@ MOE_EXPORT moe_status moe_combine(const void* y, const int32_t* slot_of, const f
   if (T < 0 || k < 1 || d < 1 || !valid_dtype(dt)) return MOE_ERR_ARG;
   if (k > kMaxK || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!y || !slot_of || !gates || !out) return MOE_ERR_ARG;
+  if (!y || !slot_of || !out) return MOE_ERR_ARG;  // gates NULL: every gate is 1
   if (((size_t)d * dtype_bytes(dt)) % 16 != 0 || (uintptr_t)y % 16 || (uintptr_t)out % 16)
     return MOE_ERR_UNSUPPORTED;
   const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);

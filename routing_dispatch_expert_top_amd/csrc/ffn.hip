@@ -23,93 +23,10 @@
 //
 // fp32 path: a plain LDS-tiled FMA kernel with the same schedule.
 #include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
-
-constexpr int kXcd = 8;  // MI355X: workgroups go round-robin over 8 XCDs
-
-// Per-workgroup tile schedule: prefix of M-tiles per expert in LDS.
-struct Sched {
-  int mt_off[kMaxE + 1];
-  int wave_tot[16];
-};
-
-// Exclusive prefix (over experts) of ceil(M_e / BM); all threads participate.
-__device__ void build_schedule(Sched& sc, const int32_t* __restrict__ expert_off, int E, int BM) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int nwave = blockDim.x / kWave;
-  // blockDim.x >= 256 >= E: one expert per thread
-  const int e = threadIdx.x;
-  int v = 0;
-  if (e < E) {
-    const int m = expert_off[e + 1] - expert_off[e];
-    v = m > 0 ? (m + BM - 1) / BM : 0;
-  }
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += o;
-  }
-  if (lane == kWave - 1) sc.wave_tot[wave] = incl;
-  __syncthreads();
-  int pre = 0;
-  for (int w = 0; w < wave; ++w) pre += sc.wave_tot[w];
-  if (e < E) sc.mt_off[e] = pre + incl - v;
-  if (e == E - 1) sc.mt_off[E] = pre + incl;
-  (void)nwave;
-  __syncthreads();
-}
-
-// Logical tile index for this block, or -1. Consecutive logical tiles share
-// an XCD: block i runs on XCD i % 8, and XCD x takes tiles [x*q, (x+1)*q).
-__device__ __forceinline__ int xcd_logical_tile(int total) {
-  const int i = blockIdx.x;
-  const int q = (total + kXcd - 1) / kXcd;
-  const int slot = i / kXcd;
-  const int logical = (i % kXcd) * q + slot;
-  if (slot >= q || logical >= total) return -1;
-  return logical;
-}
-
-// Tile order inside an expert: blocks of kMBlock m-tiles; within a block,
-// n-tiles outer and m-tiles inner. Consecutive tiles (which start close
-// together on one XCD) share a weight panel, and an activation tile comes
-// back kMBlock tiles later, while its slices are still in the XCD's L2. With
-// m-tiles innermost over a whole expert, a large expert's activation tiles
-// would come back only after all of its m-tiles, long evicted.
-constexpr int kMBlock = 4;
-
-// tile -> (expert, n-tile, m-tile)
-__device__ __forceinline__ void decode_tile(const Sched& sc, int E, int NT, int tile, int& e,
-                                            int& nt, int& mt) {
-  int lo = 0, hi = E - 1;  // last e with mt_off[e] * NT <= tile
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (sc.mt_off[mid] * NT <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  e = lo;
-  const int rem = tile - sc.mt_off[e] * NT;
-  const int mte = sc.mt_off[e + 1] - sc.mt_off[e];
-  const int b = rem / (kMBlock * NT);        // m-block
-  const int bm = min(kMBlock, mte - b * kMBlock);  // m-tiles in this block
-  const int within = rem - b * kMBlock * NT;
-  nt = within / bm;
-  mt = b * kMBlock + within % bm;
-}
-
-// silu(u) * v = u * v / (1 + e^-u), with the hardware exp2 and reciprocal
-// (about 1 ulp each: far below the bf16 rounding of h and the fp32 tolerance).
-// Six VALU operations instead of the ~20 of a full-precision exp and an IEEE
-// division; e^-u overflowing to inf gives -0 for large negative u, as the
-// exact value rounds to.
-__device__ __forceinline__ float silu_mul(float u, float v) {
-  const float e = __builtin_amdgcn_exp2f(-u * 1.44269504088896341f);
-  return u * v * __builtin_amdgcn_rcpf(1.0f + e);
-}
 
 // ---------------------------------------------------------------- bf16 MFMA
 
@@ -182,17 +99,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
-// LDS slot of chunk c of row r when a K slice has CH 16-byte chunks per row
-// (CH = 8: 128-byte rows, CH = 4: 64-byte rows). 256 bytes of LDS cover all
-// banks; the fragment reads take 16 consecutive rows at one logical chunk,
-// and XOR-ing the chunk with the row's index among the rows sharing a bank
-// phase gives those 16 rows 16 distinct 16-byte bank groups.
-template <int CH>
-__device__ __forceinline__ int swz_ch(int r, int c) {
-  constexpr int kRowsPer256 = 16 / CH;
-  return r * CH + (c ^ ((r / kRowsPer256) & (CH - 1)));
-}
-
 // Ring stages: NSA stages of A rows and NSB stages of B rows (weights). The
 // weights get the deeper ring: they are the larger stream from HBM and
 // their misses cost the most. With NSA = 2 and NSB = 3 at 256 x 256 x 64 the
@@ -202,7 +108,8 @@ template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C) {
+    const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
+    uint16_t* __restrict__ UV) {
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
   constexpr int CH = BK / 8;           // 16-byte chunks per row of a K slice
@@ -498,6 +405,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
           pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
           pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
           *reinterpret_cast<uint2*>(crow + col) = pk;
+          if (UV) {  // training: keep u and v for the backward (row = [u | v], 2 N0 wide)
+            uint16_t* uvrow = UV + (size_t)row * (2 * N0);
+            *reinterpret_cast<uint2*>(uvrow + col) =
+                uint2{pack_bf16x2(u[4 * qd + 0], u[4 * qd + 1]), pack_bf16x2(u[4 * qd + 2], u[4 * qd + 3])};
+            *reinterpret_cast<uint2*>(uvrow + N0 + col) =
+                uint2{pack_bf16x2(v[4 * qd + 0], v[4 * qd + 1]), pack_bf16x2(v[4 * qd + 2], v[4 * qd + 3])};
+          }
         }
       }
     }
@@ -547,7 +461,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const int32_t* __restrict__ expert_off,
                                                        int E, const float* __restrict__ B0,
                                                        const float* __restrict__ B1, int K,
-                                                       int N0, float* __restrict__ C) {
+                                                       int N0, float* __restrict__ C,
+                                                       float* __restrict__ UV) {
   constexpr int BM = 64, BN = 64, BK = 16;
   constexpr int kOutCols = SWIGLU ? BN / 2 : BN;
   __shared__ float As[BK][BM + 4];
@@ -618,7 +533,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = c0 + tx * 2 + j;
-        if (col < N0) C[(size_t)row * N0 + col] = silu_mul(acc[i][j], acc[i][j + 2]);
+        if (col >= N0) continue;
+        C[(size_t)row * N0 + col] = silu_mul(acc[i][j], acc[i][j + 2]);
+        if (UV) {
+          UV[(size_t)row * (2 * N0) + col] = acc[i][j];
+          UV[(size_t)row * (2 * N0) + N0 + col] = acc[i][j + 2];
+        }
       }
     } else {
 #pragma unroll
@@ -631,14 +551,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------- launch
-
-// Upper bound of sum_e ceil(M_e / BM) for sum_e M_e = rows over E experts.
-inline int64_t mtile_upper(int64_t rows, int E, int BM) {
-  return std::min<int64_t>(rows, (rows + (int64_t)E * (BM - 1)) / BM);
-}
-inline unsigned grid_for(int64_t tiles) {
-  return (unsigned)(ceil_div(std::max<int64_t>(tiles, 1), kXcd) * kXcd);
-}
 
 // Tile shape of both launches: 256 x 256 (for gate/up, 128 gate + 128 up B
 // rows = 128 F columns), 64-wide K slices, 4 wavefronts as 2 x 2 (128 x 128
@@ -670,16 +582,16 @@ moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_
 
 using namespace moe;
 
-MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm_row,
-                                         const int32_t* expert_off, int32_t T, int32_t E,
-                                         int32_t k, int32_t d, int32_t F, const void* w_gate,
-                                         const void* w_up, moe_dtype dt, void* h,
-                                         hipStream_t stream) {
+MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t* perm_row,
+                                              const int32_t* expert_off, int32_t T, int32_t E,
+                                              int32_t k, int32_t d, int32_t F,
+                                              const void* w_gate, const void* w_up, moe_dtype dt,
+                                              void* h, void* uv, hipStream_t stream) {
   moe_status st = check_ffn(T, E, k, d, F, dt);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h) return MOE_ERR_ARG;
-  if (((uintptr_t)x_disp | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)h) % 16)
+  if (((uintptr_t)x_disp | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)h | (uintptr_t)uv) % 16)
     return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
@@ -689,15 +601,25 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
     hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, true>), dim3(grid_for(tiles)),
                        dim3(kWM * kWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
                        perm_row, expert_off, E, static_cast<const uint16_t*>(w_gate),
-                       static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h));
+                       static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h),
+                       static_cast<uint16_t*>(uv));
   } else {
     const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 32);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(tiles)), dim3(256), 0, stream,
                        static_cast<const float*>(x_disp), perm_row, expert_off, E,
                        static_cast<const float*>(w_gate), static_cast<const float*>(w_up), d, F,
-                       static_cast<float*>(h));
+                       static_cast<float*>(h), static_cast<float*>(uv));
   }
   return launch_status();
+}
+
+MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm_row,
+                                         const int32_t* expert_off, int32_t T, int32_t E,
+                                         int32_t k, int32_t d, int32_t F, const void* w_gate,
+                                         const void* w_up, moe_dtype dt, void* h,
+                                         hipStream_t stream) {
+  return moe_expert_gate_up_save(x_disp, perm_row, expert_off, T, E, k, d, F, w_gate, w_up, dt,
+                                 h, nullptr, stream);
 }
 
 MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, int32_t T,
@@ -717,12 +639,13 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
                        static_cast<const uint16_t*>(h), nullptr, expert_off, E,
                        static_cast<const uint16_t*>(w_down), nullptr, F, d,
-                       static_cast<uint16_t*>(y));
+                       static_cast<uint16_t*>(y), nullptr);
   } else {
     const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(d, 64);
     hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid_for(tiles)), dim3(256), 0, stream,
                        static_cast<const float*>(h), nullptr, expert_off, E,
-                       static_cast<const float*>(w_down), nullptr, F, d, static_cast<float*>(y));
+                       static_cast<const float*>(w_down), nullptr, F, d, static_cast<float*>(y),
+                       nullptr);
   }
   return launch_status();
 }

@@ -54,6 +54,15 @@ def lib():
                                           p, p, p]),
             "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
             "moe_plan_placement": (C.c_int, [p, p, i32, i32, i32, i32, p]),
+            "moe_expert_gate_up_save": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p,
+                                                  C.c_int, p, p, p]),
+            "moe_combine_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, C.c_int, p, p, p]),
+            "moe_expert_down_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, i32, i32, p, C.c_int,
+                                              p, p, p]),
+            "moe_expert_gate_up_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, i32, i32, p, p,
+                                                 C.c_int, p, p, p, p]),
+            "moe_dispatch_bwd": (C.c_int, [p, p, i32, i32, i32, C.c_int, p, p]),
+            "moe_route_bwd": (C.c_int, [p, p, p, i32, i32, i32, p, p]),
             "moe_shuffle_workspace_bytes": (sz, [i32, i32]),
             "moe_token_shuffle": (C.c_int, [p, i32, i32, i32, p, i32, p, i32, C.c_int, p, p, p,
                                             p, p, p, sz, p]),
@@ -245,6 +254,75 @@ def moe_grouped_ffn(x_disp, perm_row, expert_off, T, k, w_gate, w_up, w_down, h=
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), dtype_code(x_disp), _ptr(h), _ptr(y), _stream(stream)))
     return h, y
+
+
+# ---------------------------------------------------------------- backward
+
+def moe_expert_gate_up_save(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=None, uv=None,
+                            stream=None):
+    E, F, d = w_gate.shape
+    dev, dt = x_disp.device, x_disp.dtype
+    h = torch.empty((T * k, F), dtype=dt, device=dev) if h is None else h
+    uv = torch.empty((T * k, 2 * F), dtype=dt, device=dev) if uv is None else uv
+    _check("moe_expert_gate_up_save", lib().moe_expert_gate_up_save(
+        _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
+        dtype_code(x_disp), _ptr(h), _ptr(uv), _stream(stream)))
+    return h, uv
+
+
+def moe_combine_bwd(dout, y, slot_of, gates, T, k, dy=None, dgates=None, stream=None):
+    d = dout.shape[1]
+    dy = torch.empty((T * k, d), dtype=dout.dtype, device=dout.device) if dy is None else dy
+    dgates = (torch.empty((T, k), dtype=torch.float32, device=dout.device)
+              if dgates is None else dgates)
+    _check("moe_combine_bwd", lib().moe_combine_bwd(
+        _ptr(dout), _ptr(y), _ptr(slot_of), _ptr(gates), T, k, d, dtype_code(dout), _ptr(dy),
+        _ptr(dgates), _stream(stream)))
+    return dy, dgates
+
+
+def moe_expert_down_bwd(dy, h, uv, expert_off, T, k, w_down, duv=None, dw_down=None,
+                        stream=None):
+    E, d, F = w_down.shape
+    dev = dy.device
+    duv = torch.empty((T * k, 2 * F), dtype=dy.dtype, device=dev) if duv is None else duv
+    dw_down = (torch.empty((E, d, F), dtype=torch.float32, device=dev)
+               if dw_down is None else dw_down)
+    _check("moe_expert_down_bwd", lib().moe_expert_down_bwd(
+        _ptr(dy), _ptr(h), _ptr(uv), _ptr(expert_off), T, E, k, d, F, _ptr(w_down),
+        dtype_code(dy), _ptr(duv), _ptr(dw_down), _stream(stream)))
+    return duv, dw_down
+
+
+def moe_expert_gate_up_bwd(duv, x_disp, perm_row, expert_off, T, k, w_gate, w_up, da=None,
+                           dw_gate=None, dw_up=None, stream=None):
+    E, F, d = w_gate.shape
+    dev = duv.device
+    da = torch.empty((T * k, d), dtype=duv.dtype, device=dev) if da is None else da
+    f32 = dict(dtype=torch.float32, device=dev)
+    dw_gate = torch.empty((E, F, d), **f32) if dw_gate is None else dw_gate
+    dw_up = torch.empty((E, F, d), **f32) if dw_up is None else dw_up
+    _check("moe_expert_gate_up_bwd", lib().moe_expert_gate_up_bwd(
+        _ptr(duv), _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate),
+        _ptr(w_up), dtype_code(duv), _ptr(da), _ptr(dw_gate), _ptr(dw_up), _stream(stream)))
+    return da, dw_gate, dw_up
+
+
+def moe_dispatch_bwd(da, slot_of, T, k, dx=None, stream=None):
+    d = da.shape[1]
+    dx = torch.empty((T, d), dtype=da.dtype, device=da.device) if dx is None else dx
+    _check("moe_dispatch_bwd", lib().moe_dispatch_bwd(
+        _ptr(da), _ptr(slot_of), T, k, d, dtype_code(da), _ptr(dx), _stream(stream)))
+    return dx
+
+
+def moe_route_bwd(gates, dgates, topk_idx, E, dlogits=None, stream=None):
+    T, k = gates.shape
+    dlogits = (torch.empty((T, E), dtype=torch.float32, device=gates.device)
+               if dlogits is None else dlogits)
+    _check("moe_route_bwd", lib().moe_route_bwd(
+        _ptr(gates), _ptr(dgates), _ptr(topk_idx), T, E, k, _ptr(dlogits), _stream(stream)))
+    return dlogits
 
 
 def moe_plan_placement(coact, load, G, ranks_per_node=1, swap_passes=8):
