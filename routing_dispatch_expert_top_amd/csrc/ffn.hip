@@ -56,13 +56,6 @@ struct TileCfg {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
-#define MOE_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
-// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned
-#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14))
-
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Two 16-byte direct-to-LDS loads per lane. Global address of load j =
 // base + voff_j + (OFF + 1024 j) (base in SGPRs, voff_j a 32-bit per-lane

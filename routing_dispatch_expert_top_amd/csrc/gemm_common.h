@@ -7,6 +7,14 @@
 namespace moe {
 namespace {
 
+// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14))
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 constexpr int kXcd = 8;  // MI355X: workgroups go round-robin over 8 XCDs
 
 // Per-workgroup tile schedule: prefix of M-tiles per expert in LDS.
