@@ -259,25 +259,35 @@ moe_status moe_combine_bwd(const void* dout, const void* y, const int32_t* slot_
                            const float* gates, int32_t T, int32_t k, int32_t d, moe_dtype dt,
                            void* dy, float* dgates, hipStream_t stream);
 
+/* Bytes of device workspace moe_expert_down_bwd and moe_expert_gate_up_bwd
+ * need (host call, no GPU): in bf16 the weight gradients transpose their two
+ * operands into expert-padded K-contiguous rows there, so the forward's
+ * grouped GEMM computes them (about (2F + d) * (T*k + 64 E) * 2 bytes). */
+size_t moe_expert_bwd_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F);
+
 /* Down projection and SwiGLU backward, per expert e over its slots s:
  *  dh = dy[s] W_down[e];  du = dh * v * silu'(u),  dv = dh * silu(u)
  *  (silu'(u) = sg (1 + u (1 - sg)), sg = 1 / (1 + e^-u); u, v from uv);
  *  duv [T*k, 2F] (dt) out: row s = [du_s | dv_s];
  *  dw_down [E,d,F] fp32 out: dw_down[e] = sum_s dy[s] h[s]^T (zero for an
- *  expert without slots). h [T*k,F], uv [T*k,2F], w_down [E,d,F] (dt). */
+ *  expert without slots). h [T*k,F], uv [T*k,2F], w_down [E,d,F] (dt).
+ *  workspace: device scratch of at least moe_expert_bwd_workspace_bytes()
+ *  (bf16; may be NULL for fp32). */
 moe_status moe_expert_down_bwd(const void* dy, const void* h, const void* uv,
                                const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
                                int32_t d, int32_t F, const void* w_down, moe_dtype dt, void* duv,
-                               float* dw_down, hipStream_t stream);
+                               float* dw_down, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* Gate/up backward, per expert e over its slots s (a_s = x_disp[perm_row[s]]):
  *  da [T*k,d] (dt) out: da[s] = du_s W_gate[e] + dv_s W_up[e];
- *  dw_gate, dw_up [E,F,d] fp32 out: sum_s du_s a_s^T and sum_s dv_s a_s^T. */
+ *  dw_gate, dw_up [E,F,d] fp32 out: sum_s du_s a_s^T and sum_s dv_s a_s^T.
+ *  x_disp has T*k rows of capacity. workspace as for moe_expert_down_bwd. */
 moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp, const int32_t* perm_row,
                                   const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
                                   int32_t d, int32_t F, const void* w_gate, const void* w_up,
                                   moe_dtype dt, void* da, float* dw_gate, float* dw_up,
-                                  hipStream_t stream);
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch backward: dx[t] = sum_j da[slot_of[t*k+j]] (fp32 accumulation in
  * j order, stored in dt). da [T*k,d], dx [T,d]. */

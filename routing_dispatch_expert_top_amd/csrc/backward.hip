@@ -138,6 +138,102 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- padded transposes
+
+// kseg[e] = sum over e' < e of ceil(M_e' / 64) * 64 (each expert's slot count
+// rounded up to whole 64-wide K slices), kseg[E] = the padded total.
+__global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ expert_off,
+                                                          int E, int32_t* __restrict__ kseg) {
+  __shared__ Sched sc;
+  build_schedule(sc, expert_off, E, 64);
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) kseg[e] = sc.mt_off[e] * 64;
+}
+
+// dst [W][ldk] (bf16): dst[w][kseg[e] + j] = src[row(s)][w] for slot s =
+// expert_off[e] + j of expert e (row(s) = gather[s] if given), and 0 in the
+// padding columns up to kseg[e+1]. Workgroup = one 64-wide K tile (inside
+// one expert's padded segment) x 64 columns of src: 16-byte row loads into
+// LDS, transposed reads, 16-byte row stores.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(
+    const uint16_t* __restrict__ src, int ld_src, const int32_t* __restrict__ gather,
+    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ kseg, int E, int W,
+    int ldk, uint16_t* __restrict__ dst) {
+  const int col0 = blockIdx.x * 64, w0 = blockIdx.y * 64;
+  if (col0 >= kseg[E]) return;  // past every segment: never read
+  int lo = 0, hi = E - 1;       // last e with kseg[e] <= col0 (a non-empty segment)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kseg[mid] <= col0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int seg0 = expert_off[e], n_e = expert_off[e + 1] - seg0, j0 = col0 - kseg[e];
+  __shared__ uint16_t tile[64][64 + 8];  // [k][w], rows 144 bytes apart
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = tid + 256 * h, r = q >> 3, c = q & 7;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (j0 + r < n_e) {
+      const int s = seg0 + j0 + r;
+      const int row = gather ? gather[s] : s;
+      v = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld_src + w0 + c * 8);
+    }
+    *reinterpret_cast<u32x4*>(&tile[r][c * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = tid + 256 * h, wr = q >> 3, kc = q & 7;
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (uint32_t)tile[kc * 8 + 2 * i][wr] | ((uint32_t)tile[kc * 8 + 2 * i + 1][wr] << 16);
+    *reinterpret_cast<u32x4*>(dst + (size_t)(w0 + wr) * ldk + col0 + kc * 8) = v;
+  }
+}
+
+// Padded K length of the transposed operands for S slots over E experts.
+inline int64_t padded_k(int64_t S, int E) { return ceil_div(S + 63 * (int64_t)E, 64) * 64; }
+
+// Workspace of the weight-gradient path: kseg, then two transposed operands.
+struct WgradWorkspace {
+  size_t kseg, at, bt, total;
+};
+inline WgradWorkspace wgrad_workspace(int64_t S, int E, int64_t rows_a, int64_t rows_b) {
+  const int64_t ldk = padded_k(S, E);
+  WgradWorkspace w;
+  w.kseg = 0;
+  w.at = ceil_div((E + 1) * 4, 256) * 256;
+  w.bt = w.at + ceil_div(rows_a * ldk * 2, 256) * 256;
+  w.total = w.bt + ceil_div(rows_b * ldk * 2, 256) * 256;
+  return w;
+}
+
+// bf16 weight gradients through the forward's GEMM: transpose both operands
+// into expert-padded K-contiguous rows, then out[e] = at_e bt_e^T per
+// expert segment. Returns false (nothing enqueued) if the transposed
+// operands exceed the GEMM's 32-bit load offsets.
+bool wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
+                const int32_t* b_gather, int N0, const int32_t* expert_off, int E, int64_t S,
+                int msplit, float* o0, float* o1, void* workspace, hipStream_t stream) {
+  const int64_t ldk = padded_k(S, E);
+  if (!wgrad_offsets_fit(M0, N0, ldk) || ldk >= (int64_t(1) << 31)) return false;
+  const WgradWorkspace ws = wgrad_workspace(S, E, M0, N0);
+  char* w = static_cast<char*>(workspace);
+  int32_t* kseg = reinterpret_cast<int32_t*>(w + ws.kseg);
+  uint16_t* at = reinterpret_cast<uint16_t*>(w + ws.at);
+  uint16_t* bt = reinterpret_cast<uint16_t*>(w + ws.bt);
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_off, E, kseg);
+  const unsigned kt = (unsigned)(ldk / 64);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(M0 / 64)), dim3(256), 0, stream, a,
+                     lda, nullptr, expert_off, kseg, E, M0, (int)ldk, at);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(N0 / 64)), dim3(256), 0, stream, b,
+                     ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
+  launch_wgrad_bf16(at, bt, kseg, E, M0, N0, (int)ldk, msplit, o0, o1, stream);
+  return true;
+}
+
 // ---------------------------------------------------------------- GEMM descriptors
 
 enum BwdMode : int {
@@ -559,15 +655,28 @@ MOE_EXPORT moe_status moe_combine_bwd(const void* dout, const void* y, const int
   return launch_status();
 }
 
+MOE_EXPORT size_t moe_expert_bwd_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t d,
+                                                 int32_t F) {
+  if (T < 0 || E < 1 || k < 1 || d < 1 || F < 1) return 0;
+  const int64_t S = (int64_t)T * k;
+  const size_t a = wgrad_workspace(S, E, d, F).total;      // down: dy^T, h^T
+  const size_t b = wgrad_workspace(S, E, 2 * F, d).total;  // gate/up: [du dv]^T, a^T
+  return std::max(a, b);
+}
+
 MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const void* uv,
                                           const int32_t* expert_off, int32_t T, int32_t E,
                                           int32_t k, int32_t d, int32_t F, const void* w_down,
                                           moe_dtype dt, void* duv, float* dw_down,
+                                          void* workspace, size_t workspace_bytes,
                                           hipStream_t stream) {
   moe_status st = check_bwd(T, E, k, d, F, dt);
   if (st != MOE_OK) return st;
   if (!expert_off || !w_down || !dw_down || (T > 0 && (!dy || !h || !uv || !duv)))
     return MOE_ERR_ARG;
+  if (dt == MOE_BF16 &&
+      (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F)))
+    return MOE_ERR_WORKSPACE;
   if (misaligned({dy, h, uv, w_down, duv, dw_down})) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   BwdArgs p = {};
@@ -597,7 +706,10 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
   q.N0 = F;
   q.msplit = d;
   q.O0 = q.O1 = dw_down;
-  launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
+  if (dt != MOE_BF16 ||
+      !wgrad_bf16(static_cast<const uint16_t*>(dy), d, d, static_cast<const uint16_t*>(h), F,
+                  nullptr, F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream))
+    launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
   return launch_status();
 }
 
@@ -606,12 +718,16 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
                                              int32_t T, int32_t E, int32_t k, int32_t d,
                                              int32_t F, const void* w_gate, const void* w_up,
                                              moe_dtype dt, void* da, float* dw_gate,
-                                             float* dw_up, hipStream_t stream) {
+                                             float* dw_up, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_bwd(T, E, k, d, F, dt);
   if (st != MOE_OK) return st;
   if (!expert_off || !w_gate || !w_up || !dw_gate || !dw_up ||
       (T > 0 && (!duv || !x_disp || !perm_row || !da)))
     return MOE_ERR_ARG;
+  if (dt == MOE_BF16 &&
+      (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F)))
+    return MOE_ERR_WORKSPACE;
   if (misaligned({duv, x_disp, w_gate, w_up, da, dw_gate, dw_up})) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   BwdArgs p = {};
@@ -643,7 +759,11 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
   q.msplit = F;
   q.O0 = dw_gate;
   q.O1 = dw_up;
-  launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
+  if (dt != MOE_BF16 ||
+      !wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, 2 * F,
+                  static_cast<const uint16_t*>(x_disp), d, perm_row, d, expert_off, E, rows, F,
+                  dw_gate, dw_up, workspace, stream))
+    launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
   return launch_status();
 }
 

@@ -97,12 +97,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // their misses cost the most. With NSA = 2 and NSB = 3 at 256 x 256 x 64 the
 // ring is exactly the 160 KiB of LDS of a gfx950 CU, so the tile schedule is
 // built inside the ring before the first DMA lands there.
-template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU>
+// WG (weight-gradient mode): Out[e][m][n] = sum over expert e's K segment
+// [kseg[e], kseg[e+1]) of A[m][k] B0[n][k] (A: M0 rows, B0: N0 rows, both of
+// row length K, each expert's segment a multiple of BK); every expert gets
+// ceil(M0/BM) x ceil(N0/BN) tiles, rows m < msplit go to O0 (msplit x N0 per
+// expert) and the others to O1, in fp32. An expert with an empty segment
+// writes zeros.
+template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU, bool WG = false>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
-    uint16_t* __restrict__ UV) {
+    uint16_t* __restrict__ UV, const int32_t* __restrict__ kseg = nullptr, int M0 = 0,
+    int msplit = 0, float* __restrict__ O0 = nullptr, float* __restrict__ O1 = nullptr) {
+  static_assert(!(WG && SWIGLU), "weight-gradient mode has a plain epilogue");
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
   constexpr int CH = BK / 8;           // 16-byte chunks per row of a K slice
@@ -121,7 +129,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   static_assert(sizeof(Sched) <= kRing * 16, "schedule fits the ring");
 
   int e, nt, mt;
-  {
+  if (WG) {
+    const int MT = (M0 + BM - 1) / BM, NT = (N0 + BN - 1) / BN;
+    const int tile = xcd_logical_tile(E * MT * NT);
+    if (tile < 0) return;
+    e = tile / (MT * NT);
+    const int rem = tile - e * MT * NT;
+    mt = rem / NT;  // n-tiles inner: consecutive tiles share the A rows
+    nt = rem % NT;
+  } else {
     Sched& sc = *reinterpret_cast<Sched*>(ring);
     build_schedule(sc, expert_off, E, BM);
     const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
@@ -131,9 +147,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     decode_tile(sc, E, NT, tile, e, nt, mt);
     __syncthreads();  // every wave has its tile before the first DMA overwrites the schedule
   }
-  const int seg0 = expert_off[e], seg1 = expert_off[e + 1];
+  // WG: rows are A's M0 rows (the row bound plays the segment end)
+  const int seg0 = WG ? 0 : expert_off[e], seg1 = WG ? M0 : expert_off[e + 1];
   const int m0 = seg0 + mt * BM;
   const int c0 = nt * Cfg::kOutCols;
+  const int koff = WG ? kseg[e] : 0;  // first K column of the expert's segment
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -163,9 +181,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const int n = min(c0 + (b_up ? r - BN / 2 : r), N0 - 1);
     boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
   }
-  const char* a_base = reinterpret_cast<const char*>(A) - kDmaBias;
-  const char* b_base = reinterpret_cast<const char*>(b_up ? B1 : B0) +
-                       (size_t)e * N0 * krow - kDmaBias;  // expert e's panel
+  const char* a_base = reinterpret_cast<const char*>(A) + (size_t)koff * 2 - kDmaBias;
+  const char* b_base =
+      WG ? reinterpret_cast<const char*>(B0) + (size_t)koff * 2 - kDmaBias
+         : reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow -
+               kDmaBias;  // expert e's panel
   // DMA instructions i, i+1 (i even) of slice kt: i < A_INS fills A rows,
   // the rest B rows
   auto dma_ins2 = [&](int i, int kt) {
@@ -208,18 +228,20 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / BK;
+  const int KT = WG ? (kseg[e + 1] - koff) / BK : K / BK;
   // Issue order (vmcnt counts in issue order): prologue A(0), B(0), .., B(NSB-2);
   // then the DMA issued during slice kt is A(kt+1) followed by B(kt+NSB-1).
   // When slice kt is needed, only B(kt+NSB-2) (NSB = 3) may still be in flight.
+  if (!WG || KT > 0) {
 #pragma unroll
-  for (int i = 0; i < A_INS; i += 2) dma_ins2(i, 0);
+    for (int i = 0; i < A_INS; i += 2) dma_ins2(i, 0);
 #pragma unroll
-  for (int p = 0; p < NSB - 1; ++p)
-    if (p < KT) {
+    for (int p = 0; p < NSB - 1; ++p)
+      if (p < KT) {
 #pragma unroll
-      for (int i = A_INS; i < LPS; i += 2) dma_ins2(i, p);
-    }
+        for (int i = A_INS; i < LPS; i += 2) dma_ins2(i, p);
+      }
+  }
   constexpr int KS = BK / 16;  // MFMA k-steps per slice
   static_assert(KS % 2 == 0, "fragment double buffer parity");
   // Fragments are double-buffered (set (ks & 1) holds k-step ks). The last
@@ -362,7 +384,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     kstep(kCheck, 1, false, As[0], Bs[0], 0, KT, 0, 0);
   };
   static_assert(Cfg::TM <= 4, "band-count dispatch");
-  switch (tm_live) {
+  if (WG && KT == 0) {
+    // empty segment: nothing to load, the zero accumulators are written
+  } else switch (tm_live) {
     case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, (Cfg::TM >= 1 ? 1 : 0)>{}); break;
     case 2: k_loop(std::integral_constant<int, (Cfg::TM >= 2 ? 2 : 0)>{}); break;
@@ -379,7 +403,27 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   //           16-byte chunks XOR-swizzled by row, and the workgroup writes y
   //           out row by row, 16 bytes per lane (fully coalesced: y is the
   //           bigger output and scattered 8-byte stores cost more there).
-  if (SWIGLU) {
+  if (WG) {
+    // fp32 gradients: each lane's 4 consecutive columns are one 16-byte store
+#pragma unroll
+    for (int tm = 0; tm < Cfg::TM; ++tm) {
+      const int row = m0 + arow0 + tm * 32 + li;
+      if (row >= M0) continue;
+      float* orow = row < msplit ? O0 + ((size_t)e * msplit + row) * N0
+                                 : O1 + ((size_t)e * (M0 - msplit) + (row - msplit)) * N0;
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
+          if (col >= N0) continue;
+          const f32x16& a = acc[tm][tn];
+          *reinterpret_cast<f32x4*>(orow + col) =
+              f32x4{a[4 * qd + 0], a[4 * qd + 1], a[4 * qd + 2], a[4 * qd + 3]};
+        }
+      }
+    }
+  } else if (SWIGLU) {
     constexpr int half = Cfg::TN / 2;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
@@ -571,6 +615,20 @@ moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_
 }
 
 }  // namespace
+}  // namespace moe
+
+namespace moe {
+
+bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk) { return dma_offsets_fit(m0, n0, ldk); }
+
+void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg, int E, int M0,
+                       int N0, int ldk, int msplit, float* o0, float* o1, hipStream_t stream) {
+  const int64_t tiles = (int64_t)E * ceil_div(M0, kBM) * ceil_div(N0, kBN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true>),
+                     dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, at, nullptr,
+                     nullptr, E, bt, nullptr, ldk, N0, nullptr, nullptr, kseg, M0, msplit, o0, o1);
+}
+
 }  // namespace moe
 
 using namespace moe;

@@ -47,4 +47,12 @@ inline int dtype_bytes(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Weight-gradient mode of the forward's bf16 grouped GEMM (ffn.hip):
+// out[e][m][n] = sum over expert e's K segment [kseg[e], kseg[e+1]) of
+// at[m][k] bt[n][k]; at is M0 x ldk, bt is N0 x ldk (bf16, K contiguous,
+// segments multiples of 64), fp32 output split at row msplit.
+bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk);
+void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg, int E, int M0,
+                       int N0, int ldk, int msplit, float* o0, float* o1, hipStream_t stream);
+
 }  // namespace moe

@@ -57,10 +57,11 @@ def lib():
             "moe_expert_gate_up_save": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p,
                                                   C.c_int, p, p, p]),
             "moe_combine_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, C.c_int, p, p, p]),
+            "moe_expert_bwd_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
             "moe_expert_down_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, i32, i32, p, C.c_int,
-                                              p, p, p]),
+                                              p, p, p, sz, p]),
             "moe_expert_gate_up_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, i32, i32, p, p,
-                                                 C.c_int, p, p, p, p]),
+                                                 C.c_int, p, p, p, p, sz, p]),
             "moe_dispatch_bwd": (C.c_int, [p, p, i32, i32, i32, C.c_int, p, p]),
             "moe_route_bwd": (C.c_int, [p, p, p, i32, i32, i32, p, p]),
             "moe_shuffle_workspace_bytes": (sz, [i32, i32]),
@@ -281,30 +282,42 @@ def moe_combine_bwd(dout, y, slot_of, gates, T, k, dy=None, dgates=None, stream=
     return dy, dgates
 
 
+def moe_expert_bwd_workspace_bytes(T, E, k, d, F):
+    return int(lib().moe_expert_bwd_workspace_bytes(T, E, k, d, F))
+
+
+def bwd_workspace(T, E, k, d, F, device):
+    return torch.empty(max(1, moe_expert_bwd_workspace_bytes(T, E, k, d, F)), dtype=torch.uint8,
+                       device=device)
+
+
 def moe_expert_down_bwd(dy, h, uv, expert_off, T, k, w_down, duv=None, dw_down=None,
-                        stream=None):
+                        workspace=None, stream=None):
     E, d, F = w_down.shape
     dev = dy.device
     duv = torch.empty((T * k, 2 * F), dtype=dy.dtype, device=dev) if duv is None else duv
     dw_down = (torch.empty((E, d, F), dtype=torch.float32, device=dev)
                if dw_down is None else dw_down)
+    ws = bwd_workspace(T, E, k, d, F, dev) if workspace is None else workspace
     _check("moe_expert_down_bwd", lib().moe_expert_down_bwd(
         _ptr(dy), _ptr(h), _ptr(uv), _ptr(expert_off), T, E, k, d, F, _ptr(w_down),
-        dtype_code(dy), _ptr(duv), _ptr(dw_down), _stream(stream)))
+        dtype_code(dy), _ptr(duv), _ptr(dw_down), _ptr(ws), ws.numel(), _stream(stream)))
     return duv, dw_down
 
 
 def moe_expert_gate_up_bwd(duv, x_disp, perm_row, expert_off, T, k, w_gate, w_up, da=None,
-                           dw_gate=None, dw_up=None, stream=None):
+                           dw_gate=None, dw_up=None, workspace=None, stream=None):
     E, F, d = w_gate.shape
     dev = duv.device
     da = torch.empty((T * k, d), dtype=duv.dtype, device=dev) if da is None else da
     f32 = dict(dtype=torch.float32, device=dev)
     dw_gate = torch.empty((E, F, d), **f32) if dw_gate is None else dw_gate
     dw_up = torch.empty((E, F, d), **f32) if dw_up is None else dw_up
+    ws = bwd_workspace(T, E, k, d, F, dev) if workspace is None else workspace
     _check("moe_expert_gate_up_bwd", lib().moe_expert_gate_up_bwd(
         _ptr(duv), _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate),
-        _ptr(w_up), dtype_code(duv), _ptr(da), _ptr(dw_gate), _ptr(dw_up), _stream(stream)))
+        _ptr(w_up), dtype_code(duv), _ptr(da), _ptr(dw_gate), _ptr(dw_up), _ptr(ws), ws.numel(),
+        _stream(stream)))
     return da, dw_gate, dw_up
 
 
