@@ -693,7 +693,14 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
   p.uv = static_cast<const uint16_t*>(uv);
   p.duv = static_cast<uint16_t*>(duv);
   p.F = F;
-  if (rows > 0) launch_gemm_bwd<kDgradSwiglu>(p, dt, rows, stream);
+  if (rows > 0) {
+    if (dt == MOE_BF16 && dgrad_offsets_fit(rows, d))
+      launch_dgrad_bf16(static_cast<const uint16_t*>(dy), rows, expert_off, E, d,
+                        static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(w_down),
+                        d, F, static_cast<const uint16_t*>(uv), static_cast<uint16_t*>(duv), stream);
+    else
+      launch_gemm_bwd<kDgradSwiglu>(p, dt, rows, stream);
+  }
   // dW_down[e] = dy^T h: M0 = d, N0 = F, reduction over the expert's slots
   BwdArgs q = {};
   q.expert_off = expert_off;
@@ -744,7 +751,14 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
   p.estride = (size_t)F * d;
   p.C = static_cast<uint16_t*>(da);
   p.ldc = d;
-  if (rows > 0) launch_gemm_bwd<kDgradPlain>(p, dt, rows, stream);
+  if (rows > 0) {
+    if (dt == MOE_BF16 && dgrad_offsets_fit(rows, 2 * F))
+      launch_dgrad_bf16(static_cast<const uint16_t*>(duv), rows, expert_off, E, 2 * F,
+                        static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                        F, d, nullptr, static_cast<uint16_t*>(da), stream);
+    else
+      launch_gemm_bwd<kDgradPlain>(p, dt, rows, stream);
+  }
   // [dW_gate; dW_up][e] = [du dv]^T a, a = x_disp[perm_row[s]]: M0 = 2F, N0 = d
   BwdArgs q = {};
   q.expert_off = expert_off;

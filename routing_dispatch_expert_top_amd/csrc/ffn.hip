@@ -103,7 +103,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // ceil(M0/BM) x ceil(N0/BN) tiles, rows m < msplit go to O0 (msplit x N0 per
 // expert) and the others to O1, in fp32. An expert with an empty segment
 // writes zeros.
-template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU, bool WG = false>
+// BT (transposed-weight mode, for the data gradients): B rows are K rows of
+// a [K][N0] panel (N contiguous; expert e's panel = ksplit x N0 elements of
+// B0 for k < ksplit, of B1 for k >= ksplit, with ksplit passed in msplit).
+// Its slices are DMA-loaded raw (two 512-byte K rows per 1 KiB block, the
+// 16-byte chunk index XOR-ed with 2 (row & 3)) and each B fragment is two
+// ds_read_b64_tr_b16: inside a group of 16 lanes, lane j receives element
+// j mod 4 of the 8 bytes addressed by lane 4 m + j / 4 as its value m, so
+// lanes that address K row k0 + s / 4, columns n0 + 4 (s mod 4) give lane j
+// the 4 K values of column n0 + j (checked on the device).
+// SWB (SwiGLU backward epilogue): C = [du | dv] rows of 2 N0, from the tile
+// (dh) and the saved [u | v] rows in UV.
+template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU, bool WG = false,
+          bool BT = false, bool SWB = false>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
@@ -111,6 +123,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     uint16_t* __restrict__ UV, const int32_t* __restrict__ kseg = nullptr, int M0 = 0,
     int msplit = 0, float* __restrict__ O0 = nullptr, float* __restrict__ O1 = nullptr) {
   static_assert(!(WG && SWIGLU), "weight-gradient mode has a plain epilogue");
+  static_assert(!BT || (!SWIGLU && !WG && BK == 64), "transposed-weight mode: data gradients");
+  static_assert(!SWB || BT, "SwiGLU-backward epilogue belongs to the down data gradient");
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
   constexpr int CH = BK / 8;           // 16-byte chunks per row of a K slice
@@ -176,10 +190,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = RPI * (wave * B_INS + i) + lane / CH;
-    const int c = swz_ch<CH>(r, lane % CH) - r * CH;
-    const int n = min(c0 + (b_up ? r - BN / 2 : r), N0 - 1);
-    boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
+    if (BT) {
+      // block i of the wave = K rows 2 (wave B_INS + i) + {0, 1} of the slice
+      const int r = 2 * (wave * B_INS + i) + lane / 32;
+      const int c = (lane % 32) ^ (2 * (r & 3));  // logical chunk in this physical slot
+      const int n = min(c0 + c * 8, N0 - 8);
+      boff[i] = (uint32_t)(r * N0 + n) * 2u + kDmaBias - 1024u * (i & 3);
+    } else {
+      const int r = RPI * (wave * B_INS + i) + lane / CH;
+      const int c = swz_ch<CH>(r, lane % CH) - r * CH;
+      const int n = min(c0 + (b_up ? r - BN / 2 : r), N0 - 1);
+      boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
+    }
   }
   const char* a_base = reinterpret_cast<const char*>(A) + (size_t)koff * 2 - kDmaBias;
   const char* b_base =
@@ -195,7 +217,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const u32x4* stage = is_a ? As[kt % NSA] : Bs[kt % NSB];
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(
         lds_addr(stage + RPI * (wave * ins + (ii & ~3)) * CH));
-    const char* base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
+    const char* base;
+    if (BT && !is_a) {
+      const int k0 = kt * BK;
+      const bool hi = k0 >= msplit;  // ksplit: uniform over the slice
+      base = reinterpret_cast<const char*>(hi ? B1 : B0) +
+             ((size_t)e * msplit * N0 + (size_t)(hi ? k0 - msplit : k0) * N0) * 2 - kDmaBias;
+    } else {
+      base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
+    }
     const uint32_t v0 = is_a ? aoff[ii] : boff[ii];
     const uint32_t v1 = is_a ? aoff[ii + 1] : boff[ii + 1];
     if ((ii & 3) == 0) dma_pair<0>(v0, v1, base, m0v);
@@ -219,6 +249,31 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     }
     fb_row[tn] = br + li;
   }
+  // BT: byte offset in a B stage of this lane's first transposed read of
+  // fragment tn at k-step 0 (k-step ks adds 16 K rows = 8192 bytes, the
+  // second read 4 K rows = 2048 bytes)
+  uint32_t fbt_off[Cfg::TN];
+  if (BT) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int kb = 8 * (g >> 1) + sl / 4;
+#pragma unroll
+    for (int tn = 0; tn < Cfg::TN; ++tn) {
+      const int col = wn * Cfg::kWaveCols + tn * 32 + 16 * (g & 1) + 4 * (sl % 4);
+      fbt_off[tn] = (uint32_t)(kb * 512 + (((col >> 3) ^ (2 * (kb & 3))) << 4) + (col & 7) * 2);
+    }
+  }
+  auto read_bt = [&](const u32x4* bs, int tn, int ks) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const char* b = reinterpret_cast<const char*>(bs) + fbt_off[tn] + ks * 8192;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(const lds_void_t*)(b));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(const lds_void_t*)(b + 2048));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  };
 
   f32x16 acc[Cfg::TM][Cfg::TN];
 #pragma unroll
@@ -276,6 +331,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       auto read_frag = [&](int j) {
         if (j < LIVE)
           fa[set ^ 1][j] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[j], ch)]);
+        else if (BT)
+          fb[set ^ 1][j - LIVE] = read_bt(bs, j - LIVE, ks_next);
         else
           fb[set ^ 1][j - LIVE] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[j - LIVE], ch)]);
       };
@@ -314,14 +371,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       }
       if (rd) {
         // one fragment read after each MFMA, then the remaining MFMAs (or reads)
+        // (a transposed-weight B fragment is two LDS reads)
         constexpr int NP = NM < NR ? NM : NR;
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          if (BT && i >= LIVE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+          else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // DS read
         }
+        constexpr int REM_B = BT ? (NR - (NP > LIVE ? NP : LIVE)) : 0;
+        constexpr int REM_DS = (NR - NP) + (REM_B > 0 ? REM_B : 0);
         if (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
-        if (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+        if (REM_DS > 0) __builtin_amdgcn_sched_group_barrier(0x100, REM_DS, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -333,7 +394,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         fa[0][tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn)
-        fb[0][tn] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
+        fb[0][tn] = BT ? read_bt(bs, tn, 0) : __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
     };
     auto slice_ready = [&](int kt) {  // slice kt landed; every wave is done with slice kt-1
       MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stages are refilled
@@ -403,7 +464,41 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   //           16-byte chunks XOR-swizzled by row, and the workgroup writes y
   //           out row by row, 16 bytes per lane (fully coalesced: y is the
   //           bigger output and scattered 8-byte stores cost more there).
-  if (WG) {
+  if (SWB) {
+    // SwiGLU backward: dh (the tile) with the saved u, v of the same columns
+    // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows
+#pragma unroll
+    for (int tm = 0; tm < Cfg::TM; ++tm) {
+      const int row = m0 + arow0 + tm * 32 + li;
+      if (row >= seg1) continue;
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
+          if (col >= N0) continue;
+          const size_t o = (size_t)row * (2 * N0) + col;
+          const uint2 uu = *reinterpret_cast<const uint2*>(UV + o);
+          const uint2 vv = *reinterpret_cast<const uint2*>(UV + o + N0);
+          const float u[4] = {bf16lo(uu.x), bf16hi(uu.x), bf16lo(uu.y), bf16hi(uu.y)};
+          const float v[4] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y)};
+          const f32x16& a = acc[tm][tn];
+          float du[4], dv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sg =
+                __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u[i] * 1.44269504088896341f));
+            du[i] = a[4 * qd + i] * v[i] * (sg * (1.0f + u[i] * (1.0f - sg)));
+            dv[i] = a[4 * qd + i] * (u[i] * sg);
+          }
+          *reinterpret_cast<uint2*>(C + o) =
+              uint2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          *reinterpret_cast<uint2*>(C + o + N0) =
+              uint2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+        }
+      }
+    }
+  } else if (WG) {
     // fp32 gradients: each lane's 4 consecutive columns are one 16-byte store
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
@@ -620,6 +715,24 @@ moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_
 namespace moe {
 
 bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk) { return dma_offsets_fit(m0, n0, ldk); }
+
+bool dgrad_offsets_fit(int64_t rows, int64_t k) { return dma_offsets_fit(rows, 1, k); }
+
+void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_off, int E, int K,
+                       const uint16_t* w0, const uint16_t* w1, int ksplit, int N0,
+                       const uint16_t* uv, uint16_t* c, hipStream_t stream) {
+  const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(N0, kBN);
+  if (uv)
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, false, true, true>),
+                       dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, a, nullptr,
+                       expert_off, E, w0, w1, K, N0, c, const_cast<uint16_t*>(uv), nullptr, 0,
+                       ksplit, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, false, true, false>),
+                       dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, a, nullptr,
+                       expert_off, E, w0, w1, K, N0, c, nullptr, nullptr, 0, ksplit, nullptr,
+                       nullptr);
+}
 
 void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg, int E, int M0,
                        int N0, int ldk, int msplit, float* o0, float* o1, hipStream_t stream) {

@@ -51,6 +51,14 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // out[e][m][n] = sum over expert e's K segment [kseg[e], kseg[e+1]) of
 // at[m][k] bt[n][k]; at is M0 x ldk, bt is N0 x ldk (bf16, K contiguous,
 // segments multiples of 64), fp32 output split at row msplit.
+// Data-gradient mode (ffn.hip): c[s] = a[s] W[e] for the slots s of expert
+// e, W[e] = [K][N0] bf16 (rows k < ksplit from w0's panel e of ksplit x N0,
+// the rest from w1's); with uv, the epilogue applies the SwiGLU backward and
+// c holds [du | dv] rows of 2 N0, else c is [rows][N0].
+bool dgrad_offsets_fit(int64_t rows, int64_t k);
+void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_off, int E, int K,
+                       const uint16_t* w0, const uint16_t* w1, int ksplit, int N0,
+                       const uint16_t* uv, uint16_t* c, hipStream_t stream);
 bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk);
 void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg, int E, int M0,
                        int N0, int ldk, int msplit, float* o0, float* o1, hipStream_t stream);
