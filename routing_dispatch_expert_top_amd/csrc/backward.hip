@@ -12,19 +12,18 @@
 //   dispatch  dx[t] = sum_j da[slot(t,j)]
 //   routing   dlogits[t, idx[t,j]] = g_j (dg_j - sum_i g_i dg_i), else 0
 //
-// gfx950 mapping of the two GEMM shapes:
-//   data gradients: rows = an expert's slots (ragged), the weight panel is
-//     read with its output dimension contiguous ([K][N] rows);
-//   weight gradients: the reduction runs over an expert's slots (ragged K),
-//     both operands have their output dimension contiguous.
-// Both use one register-staged MFMA kernel: each thread fetches 8 rows x 16
-// bytes of an operand whose K index is the row, transposes that 8 x 8 bf16
-// block in registers (byte permutes), and writes 8 K-contiguous 16-byte
-// chunks into LDS; operands that are already K-contiguous go straight in.
-// The LDS image and the fragment reads are those of the forward kernel
-// (XOR-swizzled 16-byte chunks), the MFMA is v_mfma_f32_32x32x16_bf16 with
-// fp32 accumulation, and the next K slice is fetched into registers while
-// the current one is multiplied.
+// gfx950 mapping of the two GEMM shapes (bf16), both on the forward's DMA
+// grouped GEMM (ffn.hip):
+//   data gradients: rows = an expert's slots; the weight panel is read as
+//     [K][N] (output dimension contiguous): its slices are DMA-loaded raw and
+//     the MFMA fragments come from gfx950's transposing LDS reads; the down
+//     data gradient applies the SwiGLU backward in its epilogue;
+//   weight gradients: the reduction runs over an expert's slots, so both
+//     operands are first transposed into K-contiguous rows with each
+//     expert's slot range zero-padded to whole 64-wide K slices
+//     (transpose_pad_kernel, through LDS), and a weight-gradient mode of the
+//     same GEMM walks each expert's K segment, writing fp32.
+// fp32 uses plain LDS-tiled FMA kernels for every GEMM.
 #include "moe_internal.h"
 #include "gemm_common.h"
 
@@ -210,15 +209,21 @@ inline WgradWorkspace wgrad_workspace(int64_t S, int E, int64_t rows_a, int64_t 
   return w;
 }
 
+// The bf16 expert GEMMs of the backward load through 32-bit offsets: the
+// activation-side operands (rows x K) and the expert-padded transposes.
+bool bwd_bf16_fits(int64_t S, int E, int64_t k_dgrad, int64_t m0, int64_t n0) {
+  const int64_t ldk = padded_k(S, E);
+  return dgrad_offsets_fit(S, k_dgrad) && wgrad_offsets_fit(m0, n0, ldk) &&
+         ldk < (int64_t(1) << 31);
+}
+
 // bf16 weight gradients through the forward's GEMM: transpose both operands
 // into expert-padded K-contiguous rows, then out[e] = at_e bt_e^T per
-// expert segment. Returns false (nothing enqueued) if the transposed
-// operands exceed the GEMM's 32-bit load offsets.
-bool wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
+// expert segment.
+void wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
                 const int32_t* b_gather, int N0, const int32_t* expert_off, int E, int64_t S,
                 int msplit, float* o0, float* o1, void* workspace, hipStream_t stream) {
   const int64_t ldk = padded_k(S, E);
-  if (!wgrad_offsets_fit(M0, N0, ldk) || ldk >= (int64_t(1) << 31)) return false;
   const WgradWorkspace ws = wgrad_workspace(S, E, M0, N0);
   char* w = static_cast<char*>(workspace);
   int32_t* kseg = reinterpret_cast<int32_t*>(w + ws.kseg);
@@ -231,10 +236,9 @@ bool wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(N0 / 64)), dim3(256), 0, stream, b,
                      ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
   launch_wgrad_bf16(at, bt, kseg, E, M0, N0, (int)ldk, msplit, o0, o1, stream);
-  return true;
 }
 
-// ---------------------------------------------------------------- GEMM descriptors
+// ---------------------------------------------------------------- fp32 GEMM descriptors
 
 enum BwdMode : int {
   kDgradSwiglu = 0,  // dh = dy W_down[e]; epilogue: SwiGLU backward -> du, dv
@@ -270,233 +274,10 @@ struct BwdArgs {
   float* O1;
 };
 
-// 8 x 8 transpose of bf16: r[i] holds 8 values of K row i (8 consecutive
-// M/N indices); o[c] gets the 8 K values of index c ^ flip (flip = 0 or 1,
-// per lane). Word q of o[c] packs K rows 2q (low half) and 2q+1 (high
-// half); v_perm_b32 picks the half of the index from each (byte selector
-// 0x05040100: both low halves, 0x07060302: both high halves). Indices c and
-// c ^ 1 share their source words, so flipping only swaps the two selectors.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8], bool flip) {
-  const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
-  const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? sel_odd : sel_even;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[c][q] = __builtin_amdgcn_perm(r[2 * q + 1][c >> 1], r[2 * q][c >> 1], sel);
-  }
-}
-
 __device__ __forceinline__ void silu_parts(float u, float& silu, float& dsilu) {
   const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * 1.44269504088896341f));
   silu = u * sg;
   dsilu = sg * (1.0f + u * (1.0f - sg));
-}
-
-// ---------------------------------------------------------------- bf16 MFMA GEMM
-
-constexpr int kBBM = 256, kBBN = 256, kBBK = 64;  // tile; 4 waves as 2 x 2 of 128 x 128
-constexpr int kBCH = kBBK / 8;                     // 16-byte chunks per LDS row
-
-template <int MODE>
-__global__ __launch_bounds__(256) void gemm_bwd_bf16_kernel(BwdArgs p) {
-  constexpr int BM = kBBM, BN = kBBN, BK = kBBK, CH = kBCH;
-  constexpr int TM = 4, TN = 4;
-  __shared__ u32x4 lds[2][(BM + BN) * CH];  // 128 KiB: two stages of A then B rows
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-
-  // ---- tile
-  int e, mt, nt, seg0, seg1, m0, c0, KT;
-  if (MODE != kWgrad) {
-    Sched& sc = *reinterpret_cast<Sched*>(&lds[0][0]);
-    build_schedule(sc, p.expert_off, p.E, BM);
-    const int NT = (p.N0 + BN - 1) / BN;
-    const int tile = xcd_logical_tile(sc.mt_off[p.E] * NT);
-    if (tile < 0) return;
-    decode_tile(sc, p.E, NT, tile, e, nt, mt);
-    __syncthreads();
-    seg0 = p.expert_off[e];
-    seg1 = p.expert_off[e + 1];
-    m0 = seg0 + mt * BM;
-    c0 = nt * BN;
-    KT = p.K / BK;
-  } else {
-    const int MT = (p.M0 + BM - 1) / BM, NT = (p.N0 + BN - 1) / BN;
-    const int tile = xcd_logical_tile(p.E * MT * NT);
-    if (tile < 0) return;
-    e = tile / (MT * NT);
-    const int rem = tile - e * MT * NT;
-    mt = rem / NT;
-    nt = rem % NT;
-    seg0 = p.expert_off[e];
-    seg1 = p.expert_off[e + 1];
-    m0 = mt * BM;
-    c0 = nt * BN;
-    KT = (seg1 - seg0 + BK - 1) / BK;
-  }
-
-  // ---- global -> registers
-  // K-contiguous operand (data-gradient A): thread -> chunk tid % 8 of rows
-  // tid / 8 + 32 i. Row-major operands with K as the row: thread -> 8 x 8
-  // block (K group kg = tid % 8, index chunk nc = tid / 8).
-  const int kg = tid & 7, nc = tid >> 3;
-  u32x4 ra[8], rb[8];
-  auto load = [&](int kt) {
-    const int k0 = kt * BK;
-    if (MODE != kWgrad) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = nc + 32 * i;
-        const int s = min(m0 + r, seg1 - 1);
-        ra[i] = *reinterpret_cast<const u32x4*>(p.A + (size_t)s * p.lda + k0 + kg * 8);
-      }
-      const bool hi = k0 >= p.ksplit;  // uniform over the slice (ksplit % BK == 0)
-      const uint16_t* w = (hi ? p.W1 : p.W0) + (size_t)e * p.estride;
-      const int kr = (hi ? k0 - p.ksplit : k0) + kg * 8;
-      const int n = min(c0 + nc * 8, p.N0 - 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rb[i] = *reinterpret_cast<const u32x4*>(w + (size_t)(kr + i) * p.N0 + n);
-    } else {
-      // Rows past the expert's last slot read its last slot (in bounds) and
-      // their A values are zeroed: zero times a finite B value adds nothing.
-      // All gather indices are fetched first and then all 16 data loads, so a
-      // slice costs two memory round trips, not one per row.
-      const int m = min(m0 + nc * 8, p.M0 - 8);
-      const int n = min(c0 + nc * 8, p.N0 - 8);
-      int srow[8], brow[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) srow[i] = min(seg0 + k0 + kg * 8 + i, seg1 - 1);
-      if (p.b_gather) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) brow[i] = p.b_gather[srow[i]];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) brow[i] = srow[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(p.At + (size_t)srow[i] * p.ldat + m);
-        rb[i] = *reinterpret_cast<const u32x4*>(p.Bt + (size_t)brow[i] * p.ldbt + n);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (seg0 + k0 + kg * 8 + i >= seg1) ra[i] = u32x4{0, 0, 0, 0};
-    }
-  };
-  // registers -> LDS stage. Transposed blocks: at store c a lane writes row
-  // nc * 8 + (c ^ (nc & 1)), so the 16 lanes of one LDS pass cover rows of
-  // both parities (all 16 bank groups of 256 bytes).
-  const int odd = nc & 1;
-  auto store_t = [&](u32x4* base, const u32x4 (&r)[8]) {
-    u32x4 o[8];
-    transpose8x8(r, o, odd);  // o[c] = index c ^ odd
-#pragma unroll
-    for (int c = 0; c < 8; ++c) base[swz_ch<CH>(nc * 8 + (c ^ odd), kg)] = o[c];
-  };
-  auto store = [&](int st) {
-    u32x4* As = lds[st];
-    u32x4* Bs = lds[st] + BM * CH;
-    if (MODE != kWgrad) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) As[swz_ch<CH>(nc + 32 * i, kg)] = ra[i];
-    } else {
-      store_t(As, ra);
-    }
-    store_t(Bs, rb);
-  };
-
-  // ---- MFMA fragments: wave (wm, wn) owns rows wm*128.. of A, wn*128.. of B
-  const int wm = wave >> 1, wn = wave & 1;
-  const int li = lane & 31, lk = lane >> 5;
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  if (KT > 0) load(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    store(st);
-    __syncthreads();
-    if (kt + 1 < KT) load(kt + 1);
-    const u32x4* As = lds[st];
-    const u32x4* Bs = lds[st] + BM * CH;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + lk;
-      bf16x8 fa[TM], fb[TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        fa[tm] = __builtin_bit_cast(bf16x8, As[swz_ch<CH>(wm * 128 + tm * 32 + li, ch)]);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        fb[tn] = __builtin_bit_cast(bf16x8, Bs[swz_ch<CH>(wn * 128 + tn * 32 + li, ch)]);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          // B fragment first: lane holds 4 consecutive output columns of one row
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
-    }
-  }
-
-  // ---- epilogue: lane owns row (.. + li) and, per register quad qd, output
-  // columns 8 qd + 4 lk + 0..3 of each 32-wide column tile
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int row = m0 + wm * 128 + tm * 32 + li;
-    if (MODE != kWgrad ? row >= seg1 : row >= p.M0) continue;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int col = c0 + wn * 128 + tn * 32 + 8 * qd + 4 * lk;
-        if (col >= p.N0) continue;
-        const f32x16& a = acc[tm][tn];
-        if (MODE == kDgradPlain) {
-          uint2 pk;
-          pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
-          pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
-          *reinterpret_cast<uint2*>(p.C + (size_t)row * p.ldc + col) = pk;
-        } else if (MODE == kDgradSwiglu) {
-          const size_t o = (size_t)row * (2 * p.F) + col;
-          const uint2 uu = *reinterpret_cast<const uint2*>(p.uv + o);
-          const uint2 vv = *reinterpret_cast<const uint2*>(p.uv + o + p.F);
-          const float u[4] = {bf16lo(uu.x), bf16hi(uu.x), bf16lo(uu.y), bf16hi(uu.y)};
-          const float v[4] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y)};
-          float du[4], dv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float sl, ds;
-            silu_parts(u[i], sl, ds);
-            du[i] = a[4 * qd + i] * v[i] * ds;
-            dv[i] = a[4 * qd + i] * sl;
-          }
-          uint2 pu, pv;
-          pu.x = pack_bf16x2(du[0], du[1]);
-          pu.y = pack_bf16x2(du[2], du[3]);
-          pv.x = pack_bf16x2(dv[0], dv[1]);
-          pv.y = pack_bf16x2(dv[2], dv[3]);
-          *reinterpret_cast<uint2*>(p.duv + o) = pu;
-          *reinterpret_cast<uint2*>(p.duv + o + p.F) = pv;
-        } else {
-          float* out = row < p.msplit
-                           ? p.O0 + ((size_t)e * p.msplit + row) * p.N0
-                           : p.O1 + ((size_t)e * (p.M0 - p.msplit) + (row - p.msplit)) * p.N0;
-          *reinterpret_cast<f32x4*>(out + col) =
-              f32x4{a[4 * qd + 0], a[4 * qd + 1], a[4 * qd + 2], a[4 * qd + 3]};
-        }
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -599,21 +380,14 @@ __global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(BwdArgs p, const floa
 // ---------------------------------------------------------------- launch
 
 template <int MODE>
-void launch_gemm_bwd(const BwdArgs& p, moe_dtype dt, int64_t rows, hipStream_t stream) {
-  int64_t tiles;
-  if (dt == MOE_BF16) {
-    tiles = MODE == kWgrad ? (int64_t)p.E * ceil_div(p.M0, kBBM) * ceil_div(p.N0, kBBN)
-                           : mtile_upper(rows, p.E, kBBM) * ceil_div(p.N0, kBBN);
-    hipLaunchKernelGGL(gemm_bwd_bf16_kernel<MODE>, dim3(grid_for(tiles)), dim3(256), 0, stream, p);
-  } else {
-    tiles = MODE == kWgrad ? (int64_t)p.E * ceil_div(p.M0, 64) * ceil_div(p.N0, 64)
-                           : mtile_upper(rows, p.E, 64) * ceil_div(p.N0, 64);
-    hipLaunchKernelGGL(gemm_bwd_f32_kernel<MODE>, dim3(grid_for(tiles)), dim3(256), 0, stream, p,
-                       reinterpret_cast<const float*>(p.A), reinterpret_cast<const float*>(p.W0),
-                       reinterpret_cast<const float*>(p.W1), reinterpret_cast<float*>(p.C),
-                       reinterpret_cast<const float*>(p.uv), reinterpret_cast<float*>(p.duv),
-                       reinterpret_cast<const float*>(p.At), reinterpret_cast<const float*>(p.Bt));
-  }
+void launch_gemm_f32_bwd(const BwdArgs& p, int64_t rows, hipStream_t stream) {
+  const int64_t tiles = MODE == kWgrad ? (int64_t)p.E * ceil_div(p.M0, 64) * ceil_div(p.N0, 64)
+                                       : mtile_upper(rows, p.E, 64) * ceil_div(p.N0, 64);
+  hipLaunchKernelGGL(gemm_bwd_f32_kernel<MODE>, dim3(grid_for(tiles)), dim3(256), 0, stream, p,
+                     reinterpret_cast<const float*>(p.A), reinterpret_cast<const float*>(p.W0),
+                     reinterpret_cast<const float*>(p.W1), reinterpret_cast<float*>(p.C),
+                     reinterpret_cast<const float*>(p.uv), reinterpret_cast<float*>(p.duv),
+                     reinterpret_cast<const float*>(p.At), reinterpret_cast<const float*>(p.Bt));
 }
 
 moe_status check_bwd(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
@@ -674,15 +448,25 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
   if (st != MOE_OK) return st;
   if (!expert_off || !w_down || !dw_down || (T > 0 && (!dy || !h || !uv || !duv)))
     return MOE_ERR_ARG;
-  if (dt == MOE_BF16 &&
-      (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F)))
-    return MOE_ERR_WORKSPACE;
   if (misaligned({dy, h, uv, w_down, duv, dw_down})) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
+  if (dt == MOE_BF16) {
+    if (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F))
+      return MOE_ERR_WORKSPACE;
+    if (!bwd_bf16_fits(rows, E, d, d, F)) return MOE_ERR_UNSUPPORTED;
+    // dh = dy W_down[e] (W_down[e] = d x F = K x N0), SwiGLU backward in the epilogue
+    if (rows > 0)
+      launch_dgrad_bf16(static_cast<const uint16_t*>(dy), rows, expert_off, E, d,
+                        static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(w_down),
+                        d, F, static_cast<const uint16_t*>(uv), static_cast<uint16_t*>(duv), stream);
+    // dW_down[e] = dy^T h over the expert's slots
+    wgrad_bf16(static_cast<const uint16_t*>(dy), d, d, static_cast<const uint16_t*>(h), F, nullptr,
+               F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream);
+    return launch_status();
+  }
   BwdArgs p = {};
   p.expert_off = expert_off;
   p.E = E;
-  // dh = dy W_down[e]: W_down[e] is d x F = K x N0
   p.A = static_cast<const uint16_t*>(dy);
   p.lda = d;
   p.K = d;
@@ -693,15 +477,7 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
   p.uv = static_cast<const uint16_t*>(uv);
   p.duv = static_cast<uint16_t*>(duv);
   p.F = F;
-  if (rows > 0) {
-    if (dt == MOE_BF16 && dgrad_offsets_fit(rows, d))
-      launch_dgrad_bf16(static_cast<const uint16_t*>(dy), rows, expert_off, E, d,
-                        static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(w_down),
-                        d, F, static_cast<const uint16_t*>(uv), static_cast<uint16_t*>(duv), stream);
-    else
-      launch_gemm_bwd<kDgradSwiglu>(p, dt, rows, stream);
-  }
-  // dW_down[e] = dy^T h: M0 = d, N0 = F, reduction over the expert's slots
+  if (rows > 0) launch_gemm_f32_bwd<kDgradSwiglu>(p, rows, stream);
   BwdArgs q = {};
   q.expert_off = expert_off;
   q.E = E;
@@ -713,10 +489,7 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
   q.N0 = F;
   q.msplit = d;
   q.O0 = q.O1 = dw_down;
-  if (dt != MOE_BF16 ||
-      !wgrad_bf16(static_cast<const uint16_t*>(dy), d, d, static_cast<const uint16_t*>(h), F,
-                  nullptr, F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream))
-    launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
+  launch_gemm_f32_bwd<kWgrad>(q, rows, stream);
   return launch_status();
 }
 
@@ -732,15 +505,26 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
   if (!expert_off || !w_gate || !w_up || !dw_gate || !dw_up ||
       (T > 0 && (!duv || !x_disp || !perm_row || !da)))
     return MOE_ERR_ARG;
-  if (dt == MOE_BF16 &&
-      (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F)))
-    return MOE_ERR_WORKSPACE;
   if (misaligned({duv, x_disp, w_gate, w_up, da, dw_gate, dw_up})) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
+  if (dt == MOE_BF16) {
+    if (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F))
+      return MOE_ERR_WORKSPACE;
+    if (!bwd_bf16_fits(rows, E, 2 * F, 2 * F, d)) return MOE_ERR_UNSUPPORTED;
+    // da = du W_gate[e] + dv W_up[e]: K = 2F (rows of W_gate[e], then of W_up[e]), N0 = d
+    if (rows > 0)
+      launch_dgrad_bf16(static_cast<const uint16_t*>(duv), rows, expert_off, E, 2 * F,
+                        static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                        F, d, nullptr, static_cast<uint16_t*>(da), stream);
+    // [dW_gate; dW_up][e] = [du dv]^T a over the expert's slots, a = x_disp[perm_row[s]]
+    wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, 2 * F,
+               static_cast<const uint16_t*>(x_disp), d, perm_row, d, expert_off, E, rows, F,
+               dw_gate, dw_up, workspace, stream);
+    return launch_status();
+  }
   BwdArgs p = {};
   p.expert_off = expert_off;
   p.E = E;
-  // da = du W_gate[e] + dv W_up[e]: K = 2F (rows of W_gate[e], then of W_up[e]), N0 = d
   p.A = static_cast<const uint16_t*>(duv);
   p.lda = 2 * F;
   p.K = 2 * F;
@@ -751,15 +535,7 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
   p.estride = (size_t)F * d;
   p.C = static_cast<uint16_t*>(da);
   p.ldc = d;
-  if (rows > 0) {
-    if (dt == MOE_BF16 && dgrad_offsets_fit(rows, 2 * F))
-      launch_dgrad_bf16(static_cast<const uint16_t*>(duv), rows, expert_off, E, 2 * F,
-                        static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
-                        F, d, nullptr, static_cast<uint16_t*>(da), stream);
-    else
-      launch_gemm_bwd<kDgradPlain>(p, dt, rows, stream);
-  }
-  // [dW_gate; dW_up][e] = [du dv]^T a, a = x_disp[perm_row[s]]: M0 = 2F, N0 = d
+  if (rows > 0) launch_gemm_f32_bwd<kDgradPlain>(p, rows, stream);
   BwdArgs q = {};
   q.expert_off = expert_off;
   q.E = E;
@@ -773,11 +549,7 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
   q.msplit = F;
   q.O0 = dw_gate;
   q.O1 = dw_up;
-  if (dt != MOE_BF16 ||
-      !wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, 2 * F,
-                  static_cast<const uint16_t*>(x_disp), d, perm_row, d, expert_off, E, rows, F,
-                  dw_gate, dw_up, workspace, stream))
-    launch_gemm_bwd<kWgrad>(q, dt, rows, stream);
+  launch_gemm_f32_bwd<kWgrad>(q, rows, stream);
   return launch_status();
 }
 

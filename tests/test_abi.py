@@ -106,3 +106,22 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         ops.moe_route(torch.zeros(4, 8), 2)
+
+
+def test_backward_expert_calls_need_their_workspace():
+    """bf16 expert backward calls check their workspace before any launch
+    (pointers are never dereferenced on this path)."""
+    L = ops.lib()
+    fake = 0x10000  # 16-byte aligned, never read: the call returns first
+    T, E, k, d, F = 16, 4, 2, 64, 64
+    need = L.moe_expert_bwd_workspace_bytes(T, E, k, d, F)
+    assert need > 0
+    st = L.moe_expert_down_bwd(fake, fake, fake, fake, T, E, k, d, F, fake, ops.MOE_BF16, fake,
+                               fake, None, 0, None)
+    assert st == ops.MOE_ERR_WORKSPACE
+    st = L.moe_expert_gate_up_bwd(fake, fake, fake, fake, T, E, k, d, F, fake, fake, ops.MOE_BF16,
+                                  fake, fake, fake, fake, need - 1, None)
+    assert st == ops.MOE_ERR_WORKSPACE
+    st = L.moe_expert_down_bwd(fake, fake, fake, fake, T, E, k, 96, F, fake, ops.MOE_BF16, fake,
+                               fake, fake, need, None)
+    assert st == ops.MOE_ERR_UNSUPPORTED  # d not a multiple of 64
