@@ -141,11 +141,52 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict_
 
 // kseg[e] = sum over e' < e of ceil(M_e' / 64) * 64 (each expert's slot count
 // rounded up to whole 64-wide K slices), kseg[E] = the padded total.
+// eorder[8 * cap] (cap = ceil(E / 8)): the experts in the order the
+// weight-gradient GEMM walks them. Its tiles go to the 8 XCDs in 8
+// contiguous ranges of cap experts each, and a tile's work grows with its
+// expert's slot count, so the experts are dealt longest first to the
+// least-loaded XCD range with room left (ties: lower range); unused
+// positions hold -1.
 __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ expert_off,
-                                                          int E, int32_t* __restrict__ kseg) {
+                                                          int E, int32_t* __restrict__ kseg,
+                                                          int32_t* __restrict__ eorder) {
   __shared__ Sched sc;
+  __shared__ int32_t sorted[kMaxE];
   build_schedule(sc, expert_off, E, 64);
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) kseg[e] = sc.mt_off[e] * 64;
+  const int e = threadIdx.x;
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) kseg[i] = sc.mt_off[i] * 64;
+  if (e < E) {  // rank by padded length, longest first (ties: lower expert)
+    const int my = sc.mt_off[e + 1] - sc.mt_off[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const int len = sc.mt_off[f + 1] - sc.mt_off[f];
+      rank += len > my || (len == my && f < e);
+    }
+    sorted[rank] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  const int cap = (E + 7) / 8, lane = threadIdx.x;
+  int64_t load = 0;  // lanes 0..7: one XCD range each
+  int count = 0;
+  for (int r = 0; r < E; ++r) {
+    const int x = sorted[r];
+    const int len = sc.mt_off[x + 1] - sc.mt_off[x];
+    int64_t key = (lane < 8 && count < cap) ? (load << 8) | lane : INT64_MAX;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      const int64_t o = __shfl_xor((long long)key, off, kWave);
+      key = o < key ? o : key;
+    }
+    const int b = (int)(__shfl((long long)key, 0, kWave) & 0xFF);  // least-loaded range
+    if (lane == b) {
+      eorder[b * cap + count] = x;
+      load += len;
+      ++count;
+    }
+  }
+  if (lane < 8)
+    for (int i = count; i < cap; ++i) eorder[lane * cap + i] = -1;  // each lane its own range
 }
 
 // dst [W][ldk] (bf16): dst[w][kseg[e] + j] = src[row(s)][w] for slot s =
@@ -197,13 +238,14 @@ inline int64_t padded_k(int64_t S, int E) { return ceil_div(S + 63 * (int64_t)E,
 
 // Workspace of the weight-gradient path: kseg, then two transposed operands.
 struct WgradWorkspace {
-  size_t kseg, at, bt, total;
+  size_t kseg, eorder, at, bt, total;
 };
 inline WgradWorkspace wgrad_workspace(int64_t S, int E, int64_t rows_a, int64_t rows_b) {
   const int64_t ldk = padded_k(S, E);
   WgradWorkspace w;
   w.kseg = 0;
-  w.at = ceil_div((E + 1) * 4, 256) * 256;
+  w.eorder = ceil_div((E + 1) * 4, 256) * 256;
+  w.at = w.eorder + ceil_div(8 * ceil_div(E, 8) * 4, 256) * 256;
   w.bt = w.at + ceil_div(rows_a * ldk * 2, 256) * 256;
   w.total = w.bt + ceil_div(rows_b * ldk * 2, 256) * 256;
   return w;
@@ -227,15 +269,17 @@ void wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
   const WgradWorkspace ws = wgrad_workspace(S, E, M0, N0);
   char* w = static_cast<char*>(workspace);
   int32_t* kseg = reinterpret_cast<int32_t*>(w + ws.kseg);
+  int32_t* eorder = reinterpret_cast<int32_t*>(w + ws.eorder);
   uint16_t* at = reinterpret_cast<uint16_t*>(w + ws.at);
   uint16_t* bt = reinterpret_cast<uint16_t*>(w + ws.bt);
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_off, E, kseg);
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_off, E, kseg,
+                     eorder);
   const unsigned kt = (unsigned)(ldk / 64);
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(M0 / 64)), dim3(256), 0, stream, a,
                      lda, nullptr, expert_off, kseg, E, M0, (int)ldk, at);
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(N0 / 64)), dim3(256), 0, stream, b,
                      ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
-  launch_wgrad_bf16(at, bt, kseg, E, M0, N0, (int)ldk, msplit, o0, o1, stream);
+  launch_wgrad_bf16(at, bt, kseg, eorder, E, M0, N0, (int)ldk, msplit, o0, o1, stream);
 }
 
 // ---------------------------------------------------------------- fp32 GEMM descriptors

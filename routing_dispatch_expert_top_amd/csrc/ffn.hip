@@ -144,11 +144,16 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 
   int e, nt, mt;
   if (WG) {
+    // perm_row carries the expert order here: position p of the walk is
+    // expert perm_row[p] (-1: none), 8 ceil(E/8) positions, so each XCD's
+    // contiguous range of tiles covers whole positions
     const int MT = (M0 + BM - 1) / BM, NT = (N0 + BN - 1) / BN;
-    const int tile = xcd_logical_tile(E * MT * NT);
+    const int tile = xcd_logical_tile(8 * ((E + 7) / 8) * MT * NT);
     if (tile < 0) return;
-    e = tile / (MT * NT);
-    const int rem = tile - e * MT * NT;
+    const int pos = tile / (MT * NT);
+    e = perm_row[pos];
+    if (e < 0) return;  // uniform over the workgroup
+    const int rem = tile - pos * MT * NT;
     mt = rem / NT;  // n-tiles inner: consecutive tiles share the A rows
     nt = rem % NT;
   } else {
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const int r = RPI * (wave * A_INS + i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const int s = min(m0 + r, seg1 - 1);
-    const int src = perm_row ? perm_row[s] : s;
+    const int src = (!WG && perm_row) ? perm_row[s] : s;  // WG: perm_row is the expert order
     aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
   }
   const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
@@ -734,11 +739,12 @@ void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_of
                        nullptr);
 }
 
-void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg, int E, int M0,
-                       int N0, int ldk, int msplit, float* o0, float* o1, hipStream_t stream) {
-  const int64_t tiles = (int64_t)E * ceil_div(M0, kBM) * ceil_div(N0, kBN);
+void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
+                       const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
+                       float* o0, float* o1, hipStream_t stream) {
+  const int64_t tiles = 8 * ceil_div(E, 8) * ceil_div(M0, kBM) * ceil_div(N0, kBN);
   hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true>),
-                     dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, at, nullptr,
+                     dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, at, eorder,
                      nullptr, E, bt, nullptr, ldk, N0, nullptr, nullptr, kseg, M0, msplit, o0, o1);
 }
 

@@ -60,7 +60,10 @@ void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_of
                        const uint16_t* w0, const uint16_t* w1, int ksplit, int N0,
                        const uint16_t* uv, uint16_t* c, hipStream_t stream);
 bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk);
-void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg, int E, int M0,
-                       int N0, int ldk, int msplit, float* o0, float* o1, hipStream_t stream);
+// eorder [8 * ceil(E/8)]: expert at each position of the tile walk (-1: none);
+// XCD x takes positions [x ceil(E/8), (x+1) ceil(E/8)).
+void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
+                       const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
+                       float* o0, float* o1, hipStream_t stream);
 
 }  // namespace moe
