@@ -471,22 +471,33 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   //           bigger output and scattered 8-byte stores cost more there).
   if (SWB) {
     // SwiGLU backward: dh (the tile) with the saved u, v of the same columns
-    // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows
+    // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows.
+    // Per 32-row band every u, v load is issued first (rows and columns
+    // clamped into range), then the math and the stores (the bounds only
+    // predicate the stores), so a band costs one memory round trip.
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
       const int row = m0 + arow0 + tm * 32 + li;
+      const int rowc = min(row, seg1 - 1);
+      uint2 uu[Cfg::TN][4], vv[Cfg::TN][4];
+#pragma unroll
+      for (int tn = 0; tn < Cfg::TN; ++tn)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
+          const size_t o = (size_t)rowc * (2 * N0) + min(col, N0 - 4);
+          uu[tn][qd] = *reinterpret_cast<const uint2*>(UV + o);
+          vv[tn][qd] = *reinterpret_cast<const uint2*>(UV + o + N0);
+        }
       if (row >= seg1) continue;
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
-          if (col >= N0) continue;
-          const size_t o = (size_t)row * (2 * N0) + col;
-          const uint2 uu = *reinterpret_cast<const uint2*>(UV + o);
-          const uint2 vv = *reinterpret_cast<const uint2*>(UV + o + N0);
-          const float u[4] = {bf16lo(uu.x), bf16hi(uu.x), bf16lo(uu.y), bf16hi(uu.y)};
-          const float v[4] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y)};
+          const uint2 a2 = uu[tn][qd], b2 = vv[tn][qd];
+          const float u[4] = {bf16lo(a2.x), bf16hi(a2.x), bf16lo(a2.y), bf16hi(a2.y)};
+          const float v[4] = {bf16lo(b2.x), bf16hi(b2.x), bf16lo(b2.y), bf16hi(b2.y)};
           const f32x16& a = acc[tm][tn];
           float du[4], dv[4];
 #pragma unroll
@@ -496,10 +507,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
             du[i] = a[4 * qd + i] * v[i] * (sg * (1.0f + u[i] * (1.0f - sg)));
             dv[i] = a[4 * qd + i] * (u[i] * sg);
           }
-          *reinterpret_cast<uint2*>(C + o) =
-              uint2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-          *reinterpret_cast<uint2*>(C + o + N0) =
-              uint2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+          if (col < N0) {
+            const size_t o = (size_t)row * (2 * N0) + col;
+            *reinterpret_cast<uint2*>(C + o) =
+                uint2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+            *reinterpret_cast<uint2*>(C + o + N0) =
+                uint2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+          }
         }
       }
     }
