@@ -238,11 +238,16 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   };
 
   const int wm = wave / WN, wn = wave % WN;
-  const int arow0 = wm * Cfg::kWaveRows;
+  // The tile's 32-row MFMA bands are dealt to the WM wave rows in turn
+  // (band tm * WM + wm is this wave's tm-th), so in a tile that ends inside
+  // an expert's segment the live bands split evenly over the wave rows and
+  // the slowest wave, which sets every slice's barrier, carries about half
+  // of them rather than all of its contiguous half of the tile.
+  auto band_row = [&](int tm) { return (tm * WM + wm) * 32; };  // first tile row of band tm
   const int li = lane & 31, lk = lane >> 5;
   int fa_row[Cfg::TM], fb_row[Cfg::TN];
 #pragma unroll
-  for (int tm = 0; tm < Cfg::TM; ++tm) fa_row[tm] = arow0 + tm * 32 + li;
+  for (int tm = 0; tm < Cfg::TM; ++tm) fa_row[tm] = band_row(tm) + li;
 #pragma unroll
   for (int tn = 0; tn < Cfg::TN; ++tn) {
     int br;
@@ -314,7 +319,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   // wholly past the expert's last slot issue neither fragment reads nor
   // MFMAs. The K loop is instantiated per count (dispatched once per tile),
   // so the steady-state code has no per-band branches.
-  const int tm_live = max(0, min(Cfg::TM, (seg1 - (m0 + arow0) + 31) / 32));
+  const int nb_live = max(0, min(BM / 32, (seg1 - m0 + 31) / 32));  // the tile's live bands
+  const int tm_live = min(Cfg::TM, nb_live > wm ? (nb_live - wm + WM - 1) / WM : 0);
   bf16x8 fa[2][Cfg::TM], fb[2][Cfg::TN];
   auto k_loop = [&](auto live_c) {
     constexpr int LIVE = decltype(live_c)::value;
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     // predicate the stores), so a band costs one memory round trip.
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = m0 + arow0 + tm * 32 + li;
+      const int row = m0 + band_row(tm) + li;
       const int rowc = min(row, seg1 - 1);
       uint2 uu[Cfg::TN][4], vv[Cfg::TN][4];
 #pragma unroll
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     // fp32 gradients: each lane's 4 consecutive columns are one 16-byte store
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = m0 + arow0 + tm * 32 + li;
+      const int row = m0 + band_row(tm) + li;
       if (row >= M0) continue;
       float* orow = row < msplit ? O0 + ((size_t)e * msplit + row) * N0
                                  : O1 + ((size_t)e * (M0 - msplit) + (row - msplit)) * N0;
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     constexpr int half = Cfg::TN / 2;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = m0 + arow0 + tm * 32 + li;
+      const int row = m0 + band_row(tm) + li;
       if (row >= seg1) continue;
       uint16_t* crow = C + (size_t)row * N0;
 #pragma unroll
@@ -578,7 +584,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     };
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = arow0 + tm * 32 + li;
+      const int row = band_row(tm) + li;
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn) {
 #pragma unroll
