@@ -134,7 +134,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   constexpr int LPS = A_INS + B_INS;
   static_assert(BK == 32 || BK == 64, "K slice");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA row split");
-  static_assert(NSA == 2 && (NSB == 2 || NSB == 3), "ring depths");
+  static_assert(NSA >= 2 && NSB >= NSA, "ring depths: weights get at least as many stages");
   constexpr int kRing = (NSA * BM + NSB * BN) * CH;  // 16-byte units
   __shared__ u32x4 ring[kRing];
   u32x4 (*As)[BM * CH] = reinterpret_cast<u32x4 (*)[BM * CH]>(ring);
@@ -294,12 +294,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = WG ? (kseg[e + 1] - koff) / BK : K / BK;
-  // Issue order (vmcnt counts in issue order): prologue A(0), B(0), .., B(NSB-2);
-  // then the DMA issued during slice kt is A(kt+1) followed by B(kt+NSB-1).
-  // When slice kt is needed, only B(kt+NSB-2) (NSB = 3) may still be in flight.
+  // Issue order (vmcnt counts in issue order): prologue A(0), .., A(NSA-2),
+  // B(0), .., B(NSB-2); then the DMA issued during slice kt is A(kt+NSA-1)
+  // followed by B(kt+NSB-1), into the stages slice kt-1 used. When slice kt
+  // is needed, what was issued after A(kt) may still be in flight: B(kt+NSB-NSA)
+  // and the whole DMA of the NSA-2 slices after A(kt)'s.
   if (!WG || KT > 0) {
 #pragma unroll
-    for (int i = 0; i < A_INS; i += 2) dma_ins2(i, 0);
+    for (int p = 0; p < NSA - 1; ++p)
+      if (p < KT) {
+#pragma unroll
+        for (int i = 0; i < A_INS; i += 2) dma_ins2(i, p);
+      }
 #pragma unroll
     for (int p = 0; p < NSB - 1; ++p)
       if (p < KT) {
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
           if (q >= np) break;
           if ((NM > 0 ? q * NM / np : 0) != j) continue;
           const int i = lo + 2 * q;
-          const int nx = i < A_INS ? kt + 1 : kt + NSB - 1;
+          const int nx = i < A_INS ? kt + NSA - 1 : kt + NSB - 1;
           if (!CHK || nx < KT) dma_ins2(i, nx);
         }
       };
@@ -409,11 +415,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     };
     auto slice_ready = [&](int kt) {  // slice kt landed; every wave is done with slice kt-1
       MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stages are refilled
-      if (NSB == 3 && kt + 1 < KT) MOE_WAIT_VMCNT(B_INS);
+      // steady state: B(kt+NSB-NSA) and NSA-2 slices of DMA after A(kt), all
+      // of them issued (their last target B(kt+NSB-2) exists); after the
+      // prologue: B(1) .. B(NSB-2); otherwise nothing may stay in flight
+      constexpr int kSteady = B_INS + (NSA - 2) * (A_INS + B_INS);
+      constexpr int kFirst = (NSB - 2) * B_INS;
+      static_assert(kSteady < 64 && kFirst < 64, "vmcnt range");
+      if (kt == 0 && NSB - 2 < KT) MOE_WAIT_VMCNT(kFirst);
+      else if (kt > 0 && kt >= NSA - 1 && kt + NSB - 2 < KT) MOE_WAIT_VMCNT(kSteady);
       else MOE_WAIT_VMCNT(0);
       wg_barrier();
     };
-    // The DMA issued during slice kt (A(kt+1), then B(kt+NSB-1)) is spread
+    // The DMA issued during slice kt (A(kt+NSA-1), then B(kt+NSB-1)) is spread
     // evenly over KS k-steps: the last k-step of slice kt-1 (multiplied after
     // the barrier that frees the stages) and the first KS-1 k-steps of slice
     // kt; the last k-step is left for the loads to land.
@@ -442,15 +455,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < LPS; i += 2)
         if (i < dlo(1)) {
-          const int nx = i < A_INS ? 1 : NSB - 1;
+          const int nx = i < A_INS ? NSA - 1 : NSB - 1;
           if (nx < KT) dma_ins2(i, nx);
         }
     }
-    // steady state: while kt + 2 < KT every slice the DMA targets exists, so
-    // the loop body has no branch; the last slices check, and the last one
-    // is peeled off
+    // steady state: while kt + kLead < KT every slice the DMA of step kt
+    // targets exists (A(kt+NSA) in the share issued with its last k-step,
+    // which holds A instructions only, and B(kt+NSB-1)), so the loop body has
+    // no branch; the last slices check, and the last one is peeled off
+    static_assert(LPS / KS <= A_INS, "the first DMA share of a slice is A rows only");
+    constexpr int kLead = NSA > NSB - 1 ? NSA : NSB - 1;
     int kt = 0;
-    for (; kt + 2 < KT; ++kt) step(kNoCheck, kt);
+    for (; kt + kLead < KT; ++kt) step(kNoCheck, kt);
     for (; kt + 1 < KT; ++kt) step(kCheck, kt);
     middle_steps(kCheck, KT - 1);
     kstep(kCheck, 1, false, As[0], Bs[0], 0, KT, 0, 0);
@@ -718,6 +734,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // from LDS per MFMA than 64 x 128 ones, which matters on a power-limited chip
 // (8 waves of 64 x 128 are ~1-3% slower here).
 constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 2, kWN = 2, kNSA = 2, kNSB = 3;
+// K slice and ring depths of the forward gate/up and down launches
+constexpr int kFBK = 64, kFNSA = 2, kFNSB = 3;
 
 // The bf16 kernel addresses its operands with 32-bit per-lane byte offsets:
 // from the activation matrix (rows x K) and from one expert's weight panel
@@ -788,7 +806,8 @@ MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t*
     if (!dma_offsets_fit(rows, F, d)) return MOE_ERR_UNSUPPORTED;
     constexpr int kOut = kBN / 2;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kOut);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, true>), dim3(grid_for(tiles)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kFBK, kWM, kWN, kFNSA, kFNSB, true>),
+                       dim3(grid_for(tiles)),
                        dim3(kWM * kWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
                        perm_row, expert_off, E, static_cast<const uint16_t*>(w_gate),
                        static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h),
@@ -825,7 +844,7 @@ MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, 
   if (dt == MOE_BF16) {
     if (!dma_offsets_fit(rows, d, F)) return MOE_ERR_UNSUPPORTED;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kFBK, kWM, kWN, kFNSA, kFNSB, false>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
                        static_cast<const uint16_t*>(h), nullptr, expert_off, E,
                        static_cast<const uint16_t*>(w_down), nullptr, F, d,
