@@ -297,8 +297,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   // Issue order (vmcnt counts in issue order): prologue A(0), .., A(NSA-2),
   // B(0), .., B(NSB-2); then the DMA issued during slice kt is A(kt+NSA-1)
   // followed by B(kt+NSB-1), into the stages slice kt-1 used. When slice kt
-  // is needed, what was issued after A(kt) may still be in flight: B(kt+NSB-NSA)
-  // and the whole DMA of the NSA-2 slices after A(kt)'s.
+  // is needed, what was issued after the later of A(kt) and B(kt) may still
+  // be in flight.
   if (!WG || KT > 0) {
 #pragma unroll
     for (int p = 0; p < NSA - 1; ++p)
@@ -415,10 +415,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     };
     auto slice_ready = [&](int kt) {  // slice kt landed; every wave is done with slice kt-1
       MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stages are refilled
-      // steady state: B(kt+NSB-NSA) and NSA-2 slices of DMA after A(kt), all
-      // of them issued (their last target B(kt+NSB-2) exists); after the
-      // prologue: B(1) .. B(NSB-2); otherwise nothing may stay in flight
-      constexpr int kSteady = B_INS + (NSA - 2) * (A_INS + B_INS);
+      // steady state: the NSA-2 slices of DMA issued after the one holding
+      // A(kt), and before them, if NSB > NSA, that slice's B(kt+NSB-NSA) (when
+      // NSB = NSA it is B(kt) itself, which must have landed), all of them
+      // issued (their last target B(kt+NSB-2) exists); after the prologue:
+      // B(1) .. B(NSB-2); otherwise nothing may stay in flight
+      constexpr int kSteady = (NSB > NSA ? B_INS : 0) + (NSA - 2) * (A_INS + B_INS);
       constexpr int kFirst = (NSB - 2) * B_INS;
       static_assert(kSteady < 64 && kFirst < 64, "vmcnt range");
       if (kt == 0 && NSB - 2 < KT) MOE_WAIT_VMCNT(kFirst);
