@@ -167,8 +167,19 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     __syncthreads();  // every wave has its tile before the first DMA overwrites the schedule
   }
   // WG: rows are A's M0 rows (the row bound plays the segment end)
-  const int seg0 = WG ? 0 : expert_off[e], seg1 = WG ? M0 : expert_off[e + 1];
-  const int m0 = seg0 + mt * BM;
+  const int seg0 = WG ? 0 : expert_off[e], send = WG ? M0 : expert_off[e + 1];
+  // An expert's rows are split evenly, in whole 32-row bands, over its
+  // ceil(rows / BM) m-tiles rather than as full tiles and a short last one:
+  // the m-tiles of one weight panel then cost the same, start together and
+  // stay in step, so each weight slice is fetched into the XCD's L2 once for
+  // all of them (a short tile runs ahead and fetches the panel again).
+  int rows_per = BM;
+  if (!WG) {
+    const int me = send - seg0, nmt = (me + BM - 1) / BM;
+    rows_per = min(BM, ((me + nmt - 1) / nmt + 31) & ~31);
+  }
+  const int m0 = seg0 + mt * rows_per;
+  const int seg1 = min(send, m0 + rows_per);  // end of this tile's rows
   const int c0 = nt * Cfg::kOutCols;
   const int koff = WG ? kseg[e] : 0;  // first K column of the expert's segment
 
