@@ -628,13 +628,28 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       }
     }
     __syncthreads();
+    // Thread tid writes 16-byte chunk tid % CPR of rows tid / CPR + RSTEP p,
+    // p = 0 .. BM / RSTEP - 1. Unrolled in batches of 8 rows: 8 LDS reads in
+    // flight, then their 8 stores (a rolled loop waits out the LDS latency
+    // before every store). Rows past the tile's last slot read the ring
+    // (in range) and store nothing.
     const int rows_here = min(BM, seg1 - m0);
-    for (int q = tid; q < rows_here * CPR; q += Cfg::kThreads) {
-      const int row = q / CPR, c = q % CPR;
-      const int col = c0 + c * 8;
-      if (col >= N0) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + ot_addr(row, c * 8));
-      *reinterpret_cast<u32x4*>(C + (size_t)(m0 + row) * N0 + col) = v;
+    constexpr int RSTEP = Cfg::kThreads / CPR;
+    constexpr int NPASS = BM / RSTEP;
+    static_assert(Cfg::kThreads % CPR == 0 && BM % RSTEP == 0 && NPASS % 8 == 0, "write-back passes");
+    const int c = tid % CPR, r0 = tid / CPR;
+    const int col = c0 + c * 8;
+    uint16_t* gout = C + (size_t)(m0 + r0) * N0 + col;
+#pragma unroll
+    for (int p0 = 0; p0 < NPASS; p0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = *reinterpret_cast<const u32x4*>(ot + ot_addr(r0 + (p0 + j) * RSTEP, c * 8));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + (p0 + j) * RSTEP < rows_here && col < N0)
+          *reinterpret_cast<u32x4*>(gout + (size_t)(p0 + j) * RSTEP * N0) = v[j];
     }
   }
 }
