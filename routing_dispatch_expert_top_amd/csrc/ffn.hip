@@ -498,12 +498,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   // Epilogue. Each lane owns slot row (lane & 31) of each 32-row band and,
   // per register quad q, output columns 8q + 4*(lane>>5) + 0..3 of a 32-wide
   // column tile: 4 consecutive bf16 = one 8-byte piece.
-  //  gate/up: SwiGLU, then each piece goes straight to h (h is small; no
-  //           workgroup-wide barrier at the tile end).
-  //  down:    pieces go into a row-major tile in the (now free) LDS ring with
-  //           16-byte chunks XOR-swizzled by row, and the workgroup writes y
-  //           out row by row, 16 bytes per lane (fully coalesced: y is the
-  //           bigger output and scattered 8-byte stores cost more there).
+  //  gate/up, down: the pieces (silu(u) v for gate/up) go into a row-major
+  //           tile in the (now free) LDS ring with 16-byte chunks XOR-swizzled
+  //           by row, and the workgroup writes h or y out row by row, 16 bytes
+  //           per lane (fully coalesced; scattered 8-byte stores cost more).
+  //  gate/up keeping u and v (training): three outputs do not fit the ring;
+  //           every piece goes straight out.
   if (SWB) {
     // SwiGLU backward: dh (the tile) with the saved u, v of the same columns
     // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows.
@@ -572,13 +572,16 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         }
       }
     }
-  } else if (SWIGLU) {
+  } else if (SWIGLU && UV) {
+    // training: h and the kept u, v (row = [u | v], 2 N0 wide) go straight
+    // out as 8-byte pieces (three outputs do not fit the ring together)
     constexpr int half = Cfg::TN / 2;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm) {
       const int row = m0 + band_row(tm) + li;
       if (row >= seg1) continue;
       uint16_t* crow = C + (size_t)row * N0;
+      uint16_t* uvrow = UV + (size_t)row * (2 * N0);
 #pragma unroll
       for (int tg = 0; tg < half; ++tg) {
 #pragma unroll
@@ -591,39 +594,60 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
           pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
           pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
           *reinterpret_cast<uint2*>(crow + col) = pk;
-          if (UV) {  // training: keep u and v for the backward (row = [u | v], 2 N0 wide)
-            uint16_t* uvrow = UV + (size_t)row * (2 * N0);
-            *reinterpret_cast<uint2*>(uvrow + col) =
-                uint2{pack_bf16x2(u[4 * qd + 0], u[4 * qd + 1]), pack_bf16x2(u[4 * qd + 2], u[4 * qd + 3])};
-            *reinterpret_cast<uint2*>(uvrow + N0 + col) =
-                uint2{pack_bf16x2(v[4 * qd + 0], v[4 * qd + 1]), pack_bf16x2(v[4 * qd + 2], v[4 * qd + 3])};
-          }
+          *reinterpret_cast<uint2*>(uvrow + col) =
+              uint2{pack_bf16x2(u[4 * qd + 0], u[4 * qd + 1]), pack_bf16x2(u[4 * qd + 2], u[4 * qd + 3])};
+          *reinterpret_cast<uint2*>(uvrow + N0 + col) =
+              uint2{pack_bf16x2(v[4 * qd + 0], v[4 * qd + 1]), pack_bf16x2(v[4 * qd + 2], v[4 * qd + 3])};
         }
       }
     }
   } else {
+    // The output tile (h = silu(u) v for gate/up, y for down) is staged
+    // row-major in the freed ring, 16-byte chunks XOR-swizzled by row, and
+    // written out in whole rows, 16 bytes per lane.
     constexpr int OC = Cfg::kOutCols;  // output columns per tile
     constexpr int CPR = OC / 8;        // 16-byte chunks per output row
-    static_assert(CPR == 16 || CPR == 32, "output row chunks");
+    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "output row chunks: a power of two");
     MOE_WAIT_LGKM0();  // every wave's last fragment reads are done: the ring is free
     wg_barrier();
     char* ot = reinterpret_cast<char*>(ring);
     auto ot_addr = [&](int row, int col) {  // byte address of (row, col) in the tile
       return row * (OC * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col & 7) << 1);
     };
+    if (SWIGLU) {
+      constexpr int half = Cfg::TN / 2;
 #pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = band_row(tm) + li;
+      for (int tm = 0; tm < Cfg::TM; ++tm) {
+        const int row = band_row(tm) + li;
 #pragma unroll
-      for (int tn = 0; tn < Cfg::TN; ++tn) {
+        for (int tg = 0; tg < half; ++tg) {
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int col = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
-          const f32x16& a = acc[tm][tn];
-          uint2 pk;
-          pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
-          pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
-          *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
+          for (int qd = 0; qd < 4; ++qd) {
+            const int col = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * lk;
+            const f32x16& u = acc[tm][tg];
+            const f32x16& v = acc[tm][tg + half];
+            uint2 pk;
+            pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
+            pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
+            *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < Cfg::TM; ++tm) {
+        const int row = band_row(tm) + li;
+#pragma unroll
+        for (int tn = 0; tn < Cfg::TN; ++tn) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int col = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
+            const f32x16& a = acc[tm][tn];
+            uint2 pk;
+            pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
+            pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
+            *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
+          }
         }
       }
     }
