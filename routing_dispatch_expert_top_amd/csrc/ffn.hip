@@ -140,9 +140,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   u32x4 (*As)[BM * CH] = reinterpret_cast<u32x4 (*)[BM * CH]>(ring);
   u32x4 (*Bs)[BN * CH] = reinterpret_cast<u32x4 (*)[BN * CH]>(ring + NSA * BM * CH);
   static_assert(BM * Cfg::kOutCols * 2 <= kRing * 16, "output tile fits the ring");
-  static_assert(sizeof(Sched) <= kRing * 16, "schedule fits the ring");
+  static_assert(sizeof(TileSel) <= kRing * 16, "tile selection fits the ring");
 
-  int e, nt, mt;
+  int e = 0, nt = 0, mt = 0, sg0 = 0, sg1 = 0;
   if (WG) {
     // perm_row carries the expert order here: position p of the walk is
     // expert perm_row[p] (-1: none), 8 ceil(E/8) positions, so each XCD's
@@ -157,17 +157,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     mt = rem / NT;  // n-tiles inner: consecutive tiles share the A rows
     nt = rem % NT;
   } else {
-    Sched& sc = *reinterpret_cast<Sched*>(ring);
-    build_schedule(sc, expert_off, E, BM);
+    TileSel& ts = *reinterpret_cast<TileSel*>(ring);
     const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
-    const int total = sc.mt_off[E] * NT;
-    const int tile = xcd_logical_tile(total);
-    if (tile < 0) return;  // uniform over the workgroup
-    decode_tile(sc, E, NT, tile, e, nt, mt);
-    __syncthreads();  // every wave has its tile before the first DMA overwrites the schedule
+    if (!select_tile(ts, expert_off, E, BM, NT, e, nt, mt, sg0, sg1)) return;  // uniform
+    __syncthreads();  // every wave has its tile before the first DMA overwrites the selection
   }
   // WG: rows are A's M0 rows (the row bound plays the segment end)
-  const int seg0 = WG ? 0 : expert_off[e], send = WG ? M0 : expert_off[e + 1];
+  const int seg0 = WG ? 0 : sg0, send = WG ? M0 : sg1;
   // An expert's rows are split evenly, in whole 32-row bands, over its
   // ceil(rows / BM) m-tiles rather than as full tiles and a short last one:
   // the m-tiles of one weight panel then cost the same, start together and

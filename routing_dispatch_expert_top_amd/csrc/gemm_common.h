@@ -89,6 +89,69 @@ __device__ __forceinline__ void decode_tile(const Sched& sc, int E, int NT, int 
   mt = b * kMBlock + within % bm;
 }
 
+struct TileSel {
+  int wave_tot[16];
+  int sel[5];  // expert, its first m-tile, its m-tile count, its segment start and end
+};
+
+// This workgroup's tile of a grouped launch over ceil(M_e / BM) m-tiles per
+// expert and NT n-tiles, in the order of decode_tile and the XCD grouping of
+// xcd_logical_tile; false if the workgroup has none (uniform). Thread e
+// scans expert e's m-tiles and, holding its own prefix and segment bounds,
+// claims the tile if it falls in that expert's range, so the tile is known
+// after one LDS round instead of a search over the prefix and a reload of
+// the segment bounds. All threads take part (blockDim.x >= E).
+__device__ __forceinline__ bool select_tile(TileSel& ts, const int32_t* __restrict__ expert_off,
+                                            int E, int BM, int NT, int& e, int& nt, int& mt,
+                                            int& seg0, int& seg1) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwave = blockDim.x / kWave;
+  const int t = threadIdx.x;
+  int v = 0, o0 = 0, o1 = 0;
+  if (t < E) {
+    o0 = expert_off[t];
+    o1 = expert_off[t + 1];
+    v = (o1 - o0 + BM - 1) / BM;
+  }
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) ts.wave_tot[wave] = incl;
+  __syncthreads();
+  int pre = 0, all = 0;
+  for (int w = 0; w < nwave; ++w) {
+    const int x = ts.wave_tot[w];
+    if (w < wave) pre += x;
+    all += x;
+  }
+  const int tile = xcd_logical_tile(all * NT);
+  if (tile < 0) return false;  // uniform over the workgroup
+  const int first = pre + incl - v;  // this expert's first m-tile
+  if (t < E && v > 0 && first * NT <= tile && tile < (first + v) * NT) {
+    ts.sel[0] = t;
+    ts.sel[1] = first;
+    ts.sel[2] = v;
+    ts.sel[3] = o0;
+    ts.sel[4] = o1;
+  }
+  __syncthreads();
+  e = ts.sel[0];
+  const int mte = ts.sel[2];
+  seg0 = ts.sel[3];
+  seg1 = ts.sel[4];
+  const int rem = tile - ts.sel[1] * NT;
+  const int b = rem / (kMBlock * NT);
+  const int bm = min(kMBlock, mte - b * kMBlock);
+  const int within = rem - b * kMBlock * NT;
+  nt = within / bm;
+  mt = b * kMBlock + within % bm;
+  return true;
+}
+
 // silu(u) * v = u * v / (1 + e^-u), with the hardware exp2 and reciprocal
 // (about 1 ulp each: far below the bf16 rounding of h and the fp32 tolerance).
 // Six VALU operations instead of the ~20 of a full-precision exp and an IEEE
