@@ -167,6 +167,45 @@ def test_ffn_alone_on_oracle_layout():
     assert_close("y", host(y), y_ref, TAU["bf16"])
 
 
+
+# Segment lengths at every boundary of how a grouped launch cuts an expert's
+# rows into 256-row m-tiles of whole 32-row bands split evenly over the
+# expert: empty, one row, around one band, around one m-tile, two and three
+# m-tiles, and nine m-tiles (where the even split leaves a one-row last tile).
+SEGMENTS = [0, 1, 31, 32, 33, 255, 256, 257, 300, 511, 512, 513, 2049]
+
+
+@pytest.mark.parametrize("order", ["as_listed", "reversed"])
+def test_ffn_segment_boundaries(order):
+    rng = np.random.default_rng(11)
+    counts = SEGMENTS if order == "as_listed" else SEGMENTS[::-1]
+    E, d, F, R = len(counts), 128, 192, 3000
+    eo = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    S = int(eo[-1])
+    perm = rng.integers(0, R, S).astype(np.int32)  # each slot reads a dispatched row
+    bf = synth.f32_to_bf16_bits
+    x_disp = bf(rng.standard_normal((R, d), dtype=np.float32))
+    wg = bf(rng.standard_normal((E, F, d), dtype=np.float32) / np.sqrt(d))
+    wu = bf(rng.standard_normal((E, F, d), dtype=np.float32) / np.sqrt(d))
+    wd = bf(rng.standard_normal((E, d, F), dtype=np.float32) / np.sqrt(F))
+    y_ref, h_ref = oracle.ffn_rows(x_disp, perm, oracle.slot_experts(eo), wg, wu, wd, want_h=True)
+    # outputs start as NaN: a row no tile writes, or one written twice with
+    # another tile's rows, fails the comparison
+    h = torch.full((S, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((S, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.moe_grouped_ffn(dev(x_disp), dev(perm), dev(eo), S, 1, dev(wg), dev(wu), dev(wd), h, y)
+    torch.cuda.synchronize()
+    assert_close("h", host(h), h_ref, TAU["bf16"])
+    assert_close("y", host(y), y_ref, TAU["bf16"])
+    # per segment as well, so a short expert's rows are not hidden by the others
+    hh, yy = widen(host(h)), widen(host(y))
+    for e in range(E):
+        a, b = eo[e], eo[e + 1]
+        if b > a:
+            assert np.abs(yy[a:b] - y_ref[a:b]).max() <= TAU["bf16"] * np.abs(y_ref).max(), e
+            assert np.abs(hh[a:b] - h_ref[a:b]).max() <= TAU["bf16"] * np.abs(h_ref).max(), e
+
+
 # ------------------------------------------------------------------ full size
 
 def sampled_check(w, inp, g, n_tok=48, seed=7):
