@@ -35,21 +35,36 @@ namespace {
 // One wavefront per token: dout[t] is read once; for each choice the lane
 // chunk of y's row feeds the dot product (fp32) and the scaled dout chunk is
 // written to dy's row. dgates comes out of a wave reduction per choice.
-template <bool BF16>
+// KK > 0: k == KK at compile time (the common values), so the token's slots
+// and gates are read once into registers and every choice's y chunk is
+// loaded before any is used; KK == 0: runtime k <= kMaxK.
+template <bool BF16, int KK>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const u32x4* __restrict__ dout, const u32x4* __restrict__ y,
-    const int32_t* __restrict__ slot_of, const float* __restrict__ gates, int T, int k,
+    const int32_t* __restrict__ slot_of, const float* __restrict__ gates, int T, int k_rt,
     int row_vecs, u32x4* __restrict__ dy, float* __restrict__ dgates) {
+  constexpr int KM = KK > 0 ? KK : kMaxK;
+  const int k = KK > 0 ? KK : k_rt;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * (blockDim.x / kWave) + wave;
   if (t >= T) return;
-  float dot[kMaxK];
+  float dot[KM];
+  int sl[KM];
+  float gt[KM];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) dot[j] = 0.f;
+  for (int j = 0; j < KM; ++j) {
+    dot[j] = 0.f;
+    sl[j] = j < k ? slot_of[(size_t)t * k + j] : 0;
+    gt[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
+  }
   const u32x4* o = dout + (size_t)t * row_vecs;
   for (int c = lane; c < row_vecs; c += kWave) {
     const u32x4 ov = __builtin_nontemporal_load(o + c);
+    u32x4 yv[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) yv[j] = __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c);
     float of[8];
     if (BF16) {
 #pragma unroll
@@ -62,31 +77,29 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       for (int q = 0; q < 4; ++q) of[q] = __uint_as_float(ov[q]);
     }
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j >= k) continue;
-      const int s = slot_of[(size_t)t * k + j];
-      const float g = gates[(size_t)t * k + j];
-      const u32x4 yv = __builtin_nontemporal_load(y + (size_t)s * row_vecs + c);
+      const float g = gt[j];
       u32x4 w;
       if (BF16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          dot[j] = fmaf(of[2 * q], bf16lo(yv[q]), dot[j]);
-          dot[j] = fmaf(of[2 * q + 1], bf16hi(yv[q]), dot[j]);
+          dot[j] = fmaf(of[2 * q], bf16lo(yv[j][q]), dot[j]);
+          dot[j] = fmaf(of[2 * q + 1], bf16hi(yv[j][q]), dot[j]);
           w[q] = pack_bf16x2(g * of[2 * q], g * of[2 * q + 1]);
         }
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          dot[j] = fmaf(of[q], __uint_as_float(yv[q]), dot[j]);
+          dot[j] = fmaf(of[q], __uint_as_float(yv[j][q]), dot[j]);
           w[q] = __float_as_uint(g * of[q]);
         }
       }
-      dy[(size_t)s * row_vecs + c] = w;
+      dy[(size_t)sl[j] * row_vecs + c] = w;
     }
   }
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     if (j >= k) continue;
     float v = dot[j];
 #pragma unroll
@@ -462,14 +475,25 @@ MOE_EXPORT moe_status moe_combine_bwd(const void* dout, const void* y, const int
   if (((size_t)d * dtype_bytes(dt)) % 16 || misaligned({dout, y, dy})) return MOE_ERR_UNSUPPORTED;
   const int row_vecs = (int)((size_t)d * dtype_bytes(dt) / 16);
   const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
-  if (dt == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd_kernel<true>, grid, block, 0, stream,
+  auto launch = [&](auto bf16_c, auto kk_c) {
+    constexpr bool B = decltype(bf16_c)::value;
+    constexpr int KV = decltype(kk_c)::value;
+    hipLaunchKernelGGL((combine_bwd_kernel<B, KV>), grid, block, 0, stream,
                        static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
                        gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<false>, grid, block, 0, stream,
-                       static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
-                       gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
+  };
+  auto by_k = [&](auto bf16_c) {
+    switch (k) {
+      case 1: launch(bf16_c, std::integral_constant<int, 1>{}); break;
+      case 2: launch(bf16_c, std::integral_constant<int, 2>{}); break;
+      case 4: launch(bf16_c, std::integral_constant<int, 4>{}); break;
+      case 6: launch(bf16_c, std::integral_constant<int, 6>{}); break;
+      case 8: launch(bf16_c, std::integral_constant<int, 8>{}); break;
+      default: launch(bf16_c, std::integral_constant<int, 0>{}); break;
+    }
+  };
+  if (dt == MOE_BF16) by_k(std::true_type{});
+  else by_k(std::false_type{});
   return launch_status();
 }
 
