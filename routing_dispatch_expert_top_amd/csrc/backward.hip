@@ -205,13 +205,16 @@ __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restr
 // dst [W][ldk] (bf16): dst[w][kseg[e] + j] = src[row(s)][w] for slot s =
 // expert_off[e] + j of expert e (row(s) = gather[s] if given), and 0 in the
 // padding columns up to kseg[e+1]. Workgroup = one 64-wide K tile (inside
-// one expert's padded segment) x 64 columns of src: 16-byte row loads into
-// LDS, transposed reads, 16-byte row stores.
+// one expert's padded segment) x kTrW tiles of 64 columns of src: 16-byte
+// row loads into LDS, transposed reads, 16-byte row stores. The segment
+// search and the gathered row indices of the K tile serve all kTrW column
+// tiles (one column tile per workgroup spent most of its time on them).
+constexpr int kTrW = 4;
 __global__ __launch_bounds__(256) void transpose_pad_kernel(
     const uint16_t* __restrict__ src, int ld_src, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ kseg, int E, int W,
     int ldk, uint16_t* __restrict__ dst) {
-  const int col0 = blockIdx.x * 64, w0 = blockIdx.y * 64;
+  const int col0 = blockIdx.x * 64;
   if (col0 >= kseg[E]) return;  // past every segment: never read
   int lo = 0, hi = E - 1;       // last e with kseg[e] <= col0 (a non-empty segment)
   while (lo < hi) {
@@ -223,26 +226,35 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
   const int seg0 = expert_off[e], n_e = expert_off[e + 1] - seg0, j0 = col0 - kseg[e];
   __shared__ uint16_t tile[64][64 + 8];  // [k][w], rows 144 bytes apart
   const int tid = threadIdx.x;
+  int src_row[2];  // source row of this thread's two K rows (-1: padding)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int q = tid + 256 * h, r = q >> 3, c = q & 7;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (j0 + r < n_e) {
-      const int s = seg0 + j0 + r;
-      const int row = gather ? gather[s] : s;
-      v = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld_src + w0 + c * 8);
-    }
-    *reinterpret_cast<u32x4*>(&tile[r][c * 8]) = v;
+    const int r = (tid + 256 * h) >> 3;
+    const int s = seg0 + j0 + r;
+    src_row[h] = j0 + r < n_e ? (gather ? gather[s] : s) : -1;
   }
-  __syncthreads();
+  for (int wt = 0; wt < kTrW; ++wt) {
+    const int w0 = (blockIdx.y * kTrW + wt) * 64;
+    if (w0 >= W) break;  // uniform
+    if (wt > 0) __syncthreads();  // the previous column tile has been read out
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int q = tid + 256 * h, wr = q >> 3, kc = q & 7;
-    u32x4 v;
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + 256 * h, r = q >> 3, c = q & 7;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (src_row[h] >= 0)
+        v = *reinterpret_cast<const u32x4*>(src + (size_t)src_row[h] * ld_src + w0 + c * 8);
+      *reinterpret_cast<u32x4*>(&tile[r][c * 8]) = v;
+    }
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = (uint32_t)tile[kc * 8 + 2 * i][wr] | ((uint32_t)tile[kc * 8 + 2 * i + 1][wr] << 16);
-    *reinterpret_cast<u32x4*>(dst + (size_t)(w0 + wr) * ldk + col0 + kc * 8) = v;
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + 256 * h, wr = q >> 3, kc = q & 7;
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = (uint32_t)tile[kc * 8 + 2 * i][wr] | ((uint32_t)tile[kc * 8 + 2 * i + 1][wr] << 16);
+      *reinterpret_cast<u32x4*>(dst + (size_t)(w0 + wr) * ldk + col0 + kc * 8) = v;
+    }
   }
 }
 
@@ -288,10 +300,10 @@ void wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_off, E, kseg,
                      eorder);
   const unsigned kt = (unsigned)(ldk / 64);
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(M0 / 64)), dim3(256), 0, stream, a,
-                     lda, nullptr, expert_off, kseg, E, M0, (int)ldk, at);
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)(N0 / 64)), dim3(256), 0, stream, b,
-                     ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)ceil_div(M0 / 64, kTrW)), dim3(256), 0,
+                     stream, a, lda, nullptr, expert_off, kseg, E, M0, (int)ldk, at);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)ceil_div(N0 / 64, kTrW)), dim3(256), 0,
+                     stream, b, ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
   launch_wgrad_bf16(at, bt, kseg, eorder, E, M0, N0, (int)ldk, msplit, o0, o1, stream);
 }
 
