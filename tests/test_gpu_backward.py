@@ -116,6 +116,62 @@ def test_expert_bwd_steps(T, k, E, d, F, dtype, seed):
     assert_close("dw_up", host(dwu), rdwu, TAU[dtype])
 
 
+
+# Expert segment lengths at every boundary of the grouped launches' tiling
+# (32-row bands, 256-row m-tiles split evenly over an expert, 64-slot K tiles
+# of the weight gradients): empty, one slot, around one band, around one
+# m-tile, two and three m-tiles, nine m-tiles.
+SEGMENTS = [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 300, 511, 512, 513, 2049]
+
+
+def test_expert_bwd_segment_boundaries():
+    rng = np.random.default_rng(23)
+    E, d, F = len(SEGMENTS), 128, 192
+    eo = np.concatenate([[0], np.cumsum(SEGMENTS)]).astype(np.int32)
+    S = int(eo[-1])
+    bf = lambda a: _store(a, "bf16")
+    dy, h = bf(rng.standard_normal((S, d))), bf(rng.standard_normal((S, F)))
+    uv = bf(rng.standard_normal((S, 2 * F)) * 2)
+    wd = bf(rng.standard_normal((E, d, F)) / np.sqrt(F))
+    nan = float("nan")
+    # outputs start as NaN: a row or gradient tile no launch writes fails
+    duv = torch.full((S, 2 * F), nan, dtype=torch.bfloat16, device="cuda")
+    dwd = torch.full((E, d, F), nan, dtype=torch.float32, device="cuda")
+    ops.moe_expert_down_bwd(dev(dy), dev(h), dev(uv), dev(eo), S, 1, dev(wd), duv, dwd)
+    torch.cuda.synchronize()
+    u, v = _w(uv)[:, :F], _w(uv)[:, F:]
+    rdu, rdv, rdwd = OB.down_bwd(_w(dy), _w(h), u, v, eo, _w(wd))
+    g_duv = host(duv)
+    assert_close("du", g_duv[:, :F], rdu, TAU["bf16"])
+    assert_close("dv", g_duv[:, F:], rdv, TAU["bf16"])
+    assert_close("dw_down", host(dwd), rdwd, TAU["bf16"])
+    assert (host(dwd)[np.diff(eo) == 0] == 0).all()
+
+    R = 3000
+    x_disp = bf(rng.standard_normal((R, d)))
+    perm_row = rng.integers(0, R, size=S).astype(np.int32)
+    duv_in = bf(rng.standard_normal((S, 2 * F)))
+    wg = bf(rng.standard_normal((E, F, d)) / np.sqrt(d))
+    wu = bf(rng.standard_normal((E, F, d)) / np.sqrt(d))
+    da = torch.full((S, d), nan, dtype=torch.bfloat16, device="cuda")
+    dwg = torch.full((E, F, d), nan, dtype=torch.float32, device="cuda")
+    dwu = torch.full((E, F, d), nan, dtype=torch.float32, device="cuda")
+    ops.moe_expert_gate_up_bwd(dev(duv_in), dev(x_disp), dev(perm_row), dev(eo), S, 1, dev(wg),
+                               dev(wu), da, dwg, dwu)
+    torch.cuda.synchronize()
+    rda, rdwg, rdwu = OB.gate_up_bwd(_w(duv_in)[:, :F], _w(duv_in)[:, F:], _w(x_disp)[perm_row],
+                                     eo, _w(wg), _w(wu))
+    assert_close("da", host(da), rda, TAU["bf16"])
+    assert_close("dw_gate", host(dwg), rdwg, TAU["bf16"])
+    assert_close("dw_up", host(dwu), rdwu, TAU["bf16"])
+    # per expert as well, so a short segment's rows and gradients are not hidden by the others
+    for e in range(E):
+        a, b = eo[e], eo[e + 1]
+        tol = TAU["bf16"]
+        assert np.abs(widen(host(da))[a:b] - rda[a:b]).max(initial=0) <= tol * np.abs(rda).max(), e
+        assert np.abs(host(dwg)[e] - rdwg[e]).max() <= tol * np.abs(rdwg).max(), e
+        assert np.abs(host(dwd)[e] - rdwd[e]).max() <= tol * np.abs(rdwd).max(), e
+
 def _gpu_train_step(w, inp, dout, place):
     """Forward (saving u, v) and every backward step on the GPU."""
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
