@@ -34,11 +34,32 @@ __device__ __forceinline__ uint64_t make_key(float f, int e) {
   return ((uint64_t)ord_f32(f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// One max step against the lane the DPP control CTRL names (within a row of
+// 16 lanes), on both 32-bit halves of the key.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)phi << 32) | plo;
+  return o > x ? o : x;
+}
+
+// Max over each aligned group of L lanes, left in every lane of the group.
+// Inside a 16-lane row the partners come from DPP (quad permutes for the
+// lanes 1 and 2 away, then the half-row and row mirrors, which pair each lane
+// with one in the other half of its 8- or 16-lane group): a few cycles each
+// instead of an LDS-crossbar round trip. Wider groups take one permute per
+// doubling.
 template <int L>
 __device__ __forceinline__ uint64_t subwave_max(uint64_t x) {
+  if (L >= 2) x = dpp_max_step<0xB1>(x);   // quad_perm [1,0,3,2]
+  if (L >= 4) x = dpp_max_step<0x4E>(x);   // quad_perm [2,3,0,1]
+  if (L >= 8) x = dpp_max_step<0x141>(x);  // row_half_mirror
+  if (L >= 16) x = dpp_max_step<0x140>(x); // row_mirror
 #pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(x, off, L);
+  for (int off = 16; off < L; off <<= 1) {
+    const uint64_t o = __shfl_xor(x, off, L);
     x = o > x ? o : x;
   }
   return x;
