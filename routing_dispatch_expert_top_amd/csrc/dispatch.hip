@@ -180,9 +180,9 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
 // ascending rank order): row = base + wpre + popcount of the bits before the
 // token. Lane j < k handles choice j: its slot likewise from the expert's
 // bitmap, and the row of its expert's rank comes from the rank lane by a
-// lane shuffle. Then, if x is given, the token's row is read once (eight
-// 1 KiB blocks per step, the whole 8 KiB row at d = 4096 bf16) and written
-// to each of its rows.
+// lane shuffle. If x is given, the token's row is read once (eight 1 KiB
+// blocks per step, the whole 8 KiB row at d = 4096 bf16; the first step is
+// issued with the first index loads) and written to each of its rows.
 __global__ __launch_bounds__(256) void dispatch_token_kernel(
     const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
     const int32_t* __restrict__ rank_of, int G, const uint32_t* __restrict__ rank_mask,
@@ -202,6 +202,20 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
   const uint32_t* wm = wmask + (size_t)b * Q * kWords;
   const int32_t* wp = wpre + (size_t)b * Q * kWords;
   const uint32_t m = rank_mask[t];
+  const int e_lane = lane < k ? topk_idx[(size_t)t * k + lane] : -1;
+  // The token's row is loaded here, right behind the first index loads and
+  // before the dependent ones, so its HBM latency overlaps the row and slot
+  // computation instead of following it.
+  constexpr int U = 8;
+  const u32x4* src = x ? x + (size_t)t * row_vecs : x;
+  u32x4 v0[U];
+  if (x) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = u * kWave + lane;
+      if (c < row_vecs) v0[u] = __builtin_nontemporal_load(src + c);
+    }
+  }
   const int n = __popc(m);
   // rank lanes
   int row = 0;
@@ -215,7 +229,7 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
   // choice lanes
   int g = -1, s = 0;
   if (lane < k) {
-    const int e = topk_idx[(size_t)t * k + lane];
+    const int e = e_lane;
     if (e >= 0 && e < E) {
       const int pe = rank_of ? rank_of[(size_t)t * k + lane] : place[e];
       if (pe >= 0 && pe < G) {
@@ -233,14 +247,13 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i)
     if (i < n) dst[i] = x_disp + (size_t)__builtin_amdgcn_readlane(row, i) * row_vecs;
-  const u32x4* src = x + (size_t)t * row_vecs;
-  constexpr int U = 8;
   for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave + lane;
-      if (c < row_vecs) v[u] = __builtin_nontemporal_load(src + c);
+      if (c0 == 0) v[u] = v0[u];
+      else if (c < row_vecs) v[u] = __builtin_nontemporal_load(src + c);
     }
 #pragma unroll
     for (int i = 0; i < kMaxK; ++i) {
