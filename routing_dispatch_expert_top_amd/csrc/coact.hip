@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void coact_global_kernel(const int32_t* __rest
 
 // Largest E*T*k for the row-owner kernel: its reads of the routing result
 // grow as E*T*k (4 bytes each, from L2), the triangle kernel's work as T*k*k.
-constexpr int64_t kRowOwnerMaxWork = int64_t(1) << 24;
+constexpr int64_t kRowOwnerMaxWork = int64_t(1) << 26;
 
 int max_lds_per_block() {
   int dev = 0, v = 0;
@@ -175,10 +175,10 @@ MOE_EXPORT moe_status moe_coact_hist(const int32_t* topk_idx, int32_t T, int32_t
   if (T == 0 || k == 1) return MOE_OK;
   if (!topk_idx || !coact) return MOE_ERR_ARG;
   if ((int64_t)E * T * k <= kRowOwnerMaxWork) {
-    // about 1024 workgroups, at least 2048 entries each
+    // about 2048 workgroups, at least 2048 entries each
     const int n = T * k;
     const int chunks = (int)std::max<int64_t>(
-        1, std::min<int64_t>(ceil_div(1024, E), ceil_div(n, 2048)));
+        1, std::min<int64_t>(ceil_div(2048, E), ceil_div(n, 2048)));
     const int per_wg = (int)ceil_div(ceil_div(n, chunks), 4) * 4;
     const dim3 grid(E, (unsigned)ceil_div(n, per_wg));
     if ((uintptr_t)topk_idx % 16 == 0)

@@ -108,14 +108,15 @@ def test_coact_accumulates_and_repeats_bit_exactly():
             assert np.array_equal(o[key], outs[0][key]), key
 
 
-# (T, E, k, offset): the first four stay under the row-owner kernel's E*T*k
-# bound of 2^24 (one with the routing result 4 bytes off 16-byte alignment,
-# which takes its scalar-load variant; one with E = 4, whose workgroups see
-# about 4096 hits each, more than their LDS hit queue holds), the others
+# (T, E, k, offset): the first eight stay under the row-owner kernel's E*T*k
+# bound of 2^26 (one with the routing result 4 bytes off 16-byte alignment,
+# which takes its scalar-load variant; E = 4 and E = 2, whose workgroups see
+# thousands of hits each, more than their LDS hit queue holds), the last two
 # exceed it and take the LDS-triangle kernel; skewed draws make some cells
 # hot.
 COACT_SHAPES = [(3000, 64, 6, 0), (8192, 128, 8, 0), (2501, 48, 5, 1), (1 << 21, 4, 2, 0),
-                (50000, 64, 6, 0), (20000, 256, 8, 0), (9000, 256, 16, 0)]
+                (1 << 22, 2, 2, 0), (50000, 64, 6, 0), (20000, 256, 8, 0), (9000, 256, 16, 0),
+                (40000, 256, 8, 0), (80000, 128, 8, 0)]
 
 
 @pytest.mark.parametrize("T,E,k,off", COACT_SHAPES,
