@@ -10,8 +10,11 @@
 // most a 64-lane wavefront), each lane holding 4 consecutive logits, so one
 // 16-byte load per lane reads the row. A (logit, index) pair is packed into
 // one 64-bit key whose unsigned order is the routing order; the k rounds of
-// selection are k sub-wave max-reductions over that key (cross-lane
-// shuffles, no LDS, no atomics: the result is exact and deterministic).
+// selection are k sub-wave max-reductions over that key (DPP moves within 16
+// lanes, cross-lane shuffles beyond; no LDS, no atomics: the result is exact
+// and deterministic). When each group of the group-limited variant is a
+// power-of-two run of whole lanes, its maximum is a reduction over its own
+// lanes; other group sizes take one reduction over the token per group.
 #include "moe_internal.h"
 
 namespace moe {
@@ -65,6 +68,19 @@ __device__ __forceinline__ uint64_t subwave_max(uint64_t x) {
   return x;
 }
 
+// Max over aligned groups of `lanes` lanes (a power of two, uniform).
+__device__ __forceinline__ uint64_t lane_group_max(uint64_t x, int lanes) {
+  if (lanes >= 2) x = dpp_max_step<0xB1>(x);
+  if (lanes >= 4) x = dpp_max_step<0x4E>(x);
+  if (lanes >= 8) x = dpp_max_step<0x141>(x);
+  if (lanes >= 16) x = dpp_max_step<0x140>(x);
+  for (int off = 16; off < lanes; off <<= 1) {
+    const uint64_t o = __shfl_xor(x, off, kWave);
+    x = o > x ? o : x;
+  }
+  return x;
+}
+
 template <int L>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int n_groups, int topk_groups,
@@ -91,11 +107,31 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
   for (int v = 0; v < 4; ++v) key[v] = (active && e0 + v < E) ? make_key(val[v], e0 + v) : 0ull;
 
-  if (n_groups > 1) {
-    // group key = largest expert key of the group: its order is the order of
-    // the group maxima, ties going to the lower group (its experts have the
-    // lower indices)
-    const int gsz = E / n_groups;
+  // group key = largest expert key of the group: its order is the order of
+  // the group maxima, ties going to the lower group (its experts have the
+  // lower indices)
+  const int gsz = n_groups > 1 ? E / n_groups : E;
+  const int lpg = gsz >> 2;  // lanes per group when groups are whole lanes
+  if (n_groups > 1 && (gsz & 3) == 0 && (lpg & (lpg - 1)) == 0) {
+    // A lane's 4 logits lie in one group and group m is the aligned lanes
+    // [m lpg, (m+1) lpg) of the token, so the group key is a reduction over
+    // those lanes alone; the group's rank is read from the groups' first
+    // lanes.
+    uint64_t gk = key[0];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) gk = key[v] > gk ? key[v] : gk;
+    gk = lane_group_max(gk, lpg);
+    const int base = lane & ~(L - 1);  // the token's first lane
+    int rank = 0;
+    for (int m = 0; m < n_groups; ++m) {
+      const uint64_t o = __shfl(gk, base + m * lpg, kWave);
+      rank += o > gk ? 1 : 0;
+    }
+    if (rank >= topk_groups) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) key[v] = 0;
+    }
+  } else if (n_groups > 1) {
     uint64_t gmax[kMaxGroups];
 #pragma unroll
     for (int m = 0; m < kMaxGroups; ++m) {

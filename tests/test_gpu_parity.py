@@ -136,6 +136,32 @@ def test_coact_both_kernels(T, E, k, off):
     assert np.array_equal(host(got).astype(np.int64) - seed, ref)
 
 
+# (E, n_groups, topk_groups, k): groups of 4 to 128 experts (1 to 32 lanes of
+# 4 logits each, where a group's maximum is a reduction over its own lanes),
+# groups of 6 and 12 experts (a lane's logits in two groups; 3 lanes per
+# group), and 2 to 64 lanes per token.
+ROUTE_GROUPS = [(16, 4, 2, 3), (32, 4, 2, 4), (64, 8, 3, 6), (128, 4, 2, 8), (256, 8, 4, 8),
+                (256, 4, 1, 8), (256, 2, 1, 16), (36, 6, 3, 5), (48, 4, 3, 7), (8, 2, 1, 2)]
+
+
+@pytest.mark.parametrize("E,ng,tg,k", ROUTE_GROUPS,
+                         ids=[f"E{e}_g{g}_top{t}_k{k}" for e, g, t, k in ROUTE_GROUPS])
+def test_route_group_limited(E, ng, tg, k):
+    """Group-limited top-k, bit-exact indices: a third of the rows on a coarse
+    grid (tied logits and tied group maxima), some signed zeros, a ragged T."""
+    print(f"case route E={E} groups={ng} top_groups={tg} k={k}", flush=True)
+    rng = np.random.default_rng(E * 100 + ng * 10 + tg)
+    T = 3001
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[::3] = np.round(logits[::3] * 2.0) / 2.0
+    logits[1::7, 0] = -0.0
+    idx_ref, g_ref = oracle.route(logits, k, ng, tg)
+    idx, gates = ops.moe_route(dev(logits), k, ng, tg)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), idx_ref)
+    assert_close("gates", host(gates), g_ref, TAU_GATES)
+
+
 def test_combine_identity_experts_returns_input():
     """With y = the token's own row (identity experts), out = x up to rounding."""
     w = synth.with_shape(synth.workload(2), T=1500)
