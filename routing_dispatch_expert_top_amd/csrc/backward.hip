@@ -59,12 +59,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     gt[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
   }
   const u32x4* o = dout + (size_t)t * row_vecs;
-  for (int c = lane; c < row_vecs; c += kWave) {
-    const u32x4 ov = __builtin_nontemporal_load(o + c);
-    u32x4 yv[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < k) yv[j] = __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c);
+  // Token t walks its rows' 1 KiB blocks from block t mod nblk, wrapping
+  // around, so waves working at the same moment read different offsets of
+  // their strided rows rather than the same HBM channels; two blocks per
+  // step, all of their loads issued before any is used.
+  const int nblk = (row_vecs + kWave - 1) / kWave;
+  const int sb = t % nblk;
+  auto block = [&](int c, const u32x4& ov, const u32x4 (&yv)[KM]) {
     float of[8];
     if (BF16) {
 #pragma unroll
@@ -97,6 +98,25 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       }
       dy[(size_t)sl[j] * row_vecs + c] = w;
     }
+  };
+  for (int b = 0; b < nblk; b += 2) {
+    const int p0 = b + sb < nblk ? b + sb : b + sb - nblk;
+    const int p1 = b + 1 + sb < nblk ? b + 1 + sb : b + 1 + sb - nblk;
+    const int c0 = p0 * kWave + lane;
+    const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
+    const bool ok0 = c0 < row_vecs, ok1 = c1 < row_vecs;  // the last block may be partial
+    u32x4 ov0 = {0, 0, 0, 0}, ov1 = {0, 0, 0, 0};
+    u32x4 yv0[KM], yv1[KM];
+    if (ok0) ov0 = __builtin_nontemporal_load(o + c0);
+    if (ok1) ov1 = __builtin_nontemporal_load(o + c1);
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) {
+        yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov0;
+        yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1) : ov1;
+      }
+    if (ok0) block(c0, ov0, yv0);
+    if (ok1) block(c1, ov1, yv1);
   }
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
