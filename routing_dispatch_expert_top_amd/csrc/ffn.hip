@@ -503,48 +503,84 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   if (SWB) {
     // SwiGLU backward: dh (the tile) with the saved u, v of the same columns
     // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows.
-    // Per 32-row band every u, v load is issued first (rows and columns
-    // clamped into range), then the math and the stores (the bounds only
-    // predicate the stores), so a band costs one memory round trip.
+    // The fp32 tile goes through the freed ring in two halves of BM/2 rows
+    // (16-byte chunks XOR-swizzled by row), and the workgroup then walks
+    // whole rows: 16-byte u, v loads and du, dv stores, 8 columns per thread
+    // (direct 8-byte accesses from the MFMA layout touch 32 rows each).
+    constexpr int OC = Cfg::kOutCols;   // dh columns per tile
+    constexpr int CH4 = OC / 4;         // 16-byte fp32 chunks per staged row
+    constexpr int HR = BM / 2;          // rows per half
+    static_assert(HR * OC * 4 <= kRing * 16, "half tile fits the ring");
+    static_assert(WM == 2 && Cfg::TM == 4, "bands 2h, 2h+1 of each wave row are half h");
+    constexpr int CPR = OC / 8;                  // 8-column pieces per row
+    constexpr int RSTEP = Cfg::kThreads / CPR;   // rows per pass
+    constexpr int NB = 4;                        // rows whose loads are in flight together
+    static_assert(Cfg::kThreads % CPR == 0 && HR % (RSTEP * NB) == 0, "row passes");
+    float* st = reinterpret_cast<float*>(ring);
+    auto st_off = [&](int row, int ch) { return row * OC + ((ch ^ (row & (CH4 - 1))) << 2); };
+    const int rows_here = min(BM, seg1 - m0);
+    const int pc = tid % CPR, pr = tid / CPR;
+    const int col = c0 + pc * 8;
+    const int colc = min(col, N0 - 8);  // loads stay in the u part of the row
+    MOE_WAIT_LGKM0();  // every wave's last fragment reads are done: the ring is free
+    wg_barrier();
 #pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = m0 + band_row(tm) + li;
-      const int rowc = min(row, seg1 - 1);
-      uint2 uu[Cfg::TN][4], vv[Cfg::TN][4];
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh) __syncthreads();  // the first half has been read out
 #pragma unroll
-      for (int tn = 0; tn < Cfg::TN; ++tn)
+      for (int b = 0; b < 2; ++b) {
+        const int tm = 2 * hh + b;
+        const int row = band_row(tm) - hh * HR + li;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
-          const size_t o = (size_t)rowc * (2 * N0) + min(col, N0 - 4);
-          uu[tn][qd] = *reinterpret_cast<const uint2*>(UV + o);
-          vv[tn][qd] = *reinterpret_cast<const uint2*>(UV + o + N0);
+        for (int tn = 0; tn < Cfg::TN; ++tn) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int ch = (wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk) >> 2;
+            const f32x16& a = acc[tm][tn];
+            *reinterpret_cast<f32x4*>(st + st_off(row, ch)) =
+                f32x4{a[4 * qd + 0], a[4 * qd + 1], a[4 * qd + 2], a[4 * qd + 3]};
+          }
         }
-      if (row >= seg1) continue;
+      }
+      __syncthreads();
 #pragma unroll
-      for (int tn = 0; tn < Cfg::TN; ++tn) {
+      for (int p0 = 0; p0 < HR / RSTEP; p0 += NB) {
+        u32x4 uu[NB], vv[NB];
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
-          const uint2 a2 = uu[tn][qd], b2 = vv[tn][qd];
-          const float u[4] = {bf16lo(a2.x), bf16hi(a2.x), bf16lo(a2.y), bf16hi(a2.y)};
-          const float v[4] = {bf16lo(b2.x), bf16hi(b2.x), bf16lo(b2.y), bf16hi(b2.y)};
-          const f32x16& a = acc[tm][tn];
-          float du[4], dv[4];
+        for (int q = 0; q < NB; ++q) {
+          const int r = hh * HR + pr + (p0 + q) * RSTEP;  // tile row
+          const size_t o = (size_t)min(m0 + r, seg1 - 1) * (2 * N0) + colc;
+          uu[q] = *reinterpret_cast<const u32x4*>(UV + o);
+          vv[q] = *reinterpret_cast<const u32x4*>(UV + o + N0);
+        }
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int rh = pr + (p0 + q) * RSTEP;  // row in the half
+          const int r = hh * HR + rh;
+          if (r >= rows_here || col >= N0) continue;
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(st + st_off(rh, 2 * pc));
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(st + st_off(rh, 2 * pc + 1));
+          const float dh[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          uint32_t du2[4], dv2[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float sg =
-                __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u[i] * 1.44269504088896341f));
-            du[i] = a[4 * qd + i] * v[i] * (sg * (1.0f + u[i] * (1.0f - sg)));
-            dv[i] = a[4 * qd + i] * (u[i] * sg);
+            float du[2], dv[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float u = h2 ? bf16hi(uu[q][i]) : bf16lo(uu[q][i]);
+              const float v = h2 ? bf16hi(vv[q][i]) : bf16lo(vv[q][i]);
+              const float g = dh[2 * i + h2];
+              const float sg =
+                  __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * 1.44269504088896341f));
+              du[h2] = g * v * (sg * (1.0f + u * (1.0f - sg)));
+              dv[h2] = g * (u * sg);
+            }
+            du2[i] = pack_bf16x2(du[0], du[1]);
+            dv2[i] = pack_bf16x2(dv[0], dv[1]);
           }
-          if (col < N0) {
-            const size_t o = (size_t)row * (2 * N0) + col;
-            *reinterpret_cast<uint2*>(C + o) =
-                uint2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-            *reinterpret_cast<uint2*>(C + o + N0) =
-                uint2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
-          }
+          const size_t o = (size_t)(m0 + r) * (2 * N0) + col;
+          *reinterpret_cast<u32x4*>(C + o) = u32x4{du2[0], du2[1], du2[2], du2[3]};
+          *reinterpret_cast<u32x4*>(C + o + N0) = u32x4{dv2[0], dv2[1], dv2[2], dv2[3]};
         }
       }
     }
