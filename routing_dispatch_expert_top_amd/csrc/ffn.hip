@@ -498,8 +498,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   //           tile in the (now free) LDS ring with 16-byte chunks XOR-swizzled
   //           by row, and the workgroup writes h or y out row by row, 16 bytes
   //           per lane (fully coalesced; scattered 8-byte stores cost more).
-  //  gate/up keeping u and v (training): three outputs do not fit the ring;
-  //           every piece goes straight out.
+  //  gate/up keeping u and v (training), SwiGLU backward: the same through
+  //           the ring in two halves of BM/2 rows (a whole tile of their
+  //           outputs would not fit).
   if (SWB) {
     // SwiGLU backward: dh (the tile) with the saved u, v of the same columns
     // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows.
@@ -605,31 +606,70 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       }
     }
   } else if (SWIGLU && UV) {
-    // training: h and the kept u, v (row = [u | v], 2 N0 wide) go straight
-    // out as 8-byte pieces (three outputs do not fit the ring together)
+    // training: h and the kept u, v (row = [u | v], 2 N0 wide). The three
+    // bf16 tiles go through the freed ring in two halves of BM/2 rows (all
+    // three of a whole tile would not fit), 16-byte chunks XOR-swizzled by
+    // row, and are written out in whole rows, 16 bytes per lane.
+    constexpr int OC = Cfg::kOutCols;  // h (and u, v) columns per tile
+    constexpr int CPR = OC / 8;        // 16-byte chunks per output row
+    constexpr int HR = BM / 2;         // rows per half
+    constexpr int AB = HR * OC * 2;    // bytes of one staged half tile
+    static_assert(!SWIGLU || 3 * AB <= kRing * 16, "three half tiles fit the ring");
+    static_assert(WM == 2 && Cfg::TM == 4, "bands 2h, 2h+1 of each wave row are half h");
+    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "output row chunks: a power of two");
+    constexpr int RSTEP = Cfg::kThreads / CPR;
+    constexpr int NPASS = HR / RSTEP;
+    static_assert(Cfg::kThreads % CPR == 0 && HR % RSTEP == 0, "write-back passes");
     constexpr int half = Cfg::TN / 2;
+    char* ot = reinterpret_cast<char*>(ring);
+    auto ot_addr = [&](int row, int col) {  // byte address of (row, col) in a half tile
+      return row * (OC * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col & 7) << 1);
+    };
+    const int rows_here = min(BM, seg1 - m0);
+    const int c = tid % CPR, r0 = tid / CPR;
+    const int col = c0 + c * 8;
+    MOE_WAIT_LGKM0();  // every wave's last fragment reads are done: the ring is free
+    wg_barrier();
 #pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = m0 + band_row(tm) + li;
-      if (row >= seg1) continue;
-      uint16_t* crow = C + (size_t)row * N0;
-      uint16_t* uvrow = UV + (size_t)row * (2 * N0);
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh) __syncthreads();  // the first half has been read out
 #pragma unroll
-      for (int tg = 0; tg < half; ++tg) {
+      for (int b = 0; b < 2; ++b) {
+        const int tm = 2 * hh + b;
+        const int row = band_row(tm) - hh * HR + li;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int col = c0 + wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * lk;
-          if (col >= N0) continue;
-          const f32x16& u = acc[tm][tg];
-          const f32x16& v = acc[tm][tg + half];
-          uint2 pk;
-          pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
-          pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
-          *reinterpret_cast<uint2*>(crow + col) = pk;
-          *reinterpret_cast<uint2*>(uvrow + col) =
-              uint2{pack_bf16x2(u[4 * qd + 0], u[4 * qd + 1]), pack_bf16x2(u[4 * qd + 2], u[4 * qd + 3])};
-          *reinterpret_cast<uint2*>(uvrow + N0 + col) =
-              uint2{pack_bf16x2(v[4 * qd + 0], v[4 * qd + 1]), pack_bf16x2(v[4 * qd + 2], v[4 * qd + 3])};
+        for (int tg = 0; tg < half; ++tg) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int lc = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * lk;
+            const f32x16& u = acc[tm][tg];
+            const f32x16& v = acc[tm][tg + half];
+            uint2 pk;
+            pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
+            pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
+            const int a = ot_addr(row, lc);
+            *reinterpret_cast<uint2*>(ot + a) = pk;
+            *reinterpret_cast<uint2*>(ot + AB + a) =
+                uint2{pack_bf16x2(u[4 * qd + 0], u[4 * qd + 1]), pack_bf16x2(u[4 * qd + 2], u[4 * qd + 3])};
+            *reinterpret_cast<uint2*>(ot + 2 * AB + a) =
+                uint2{pack_bf16x2(v[4 * qd + 0], v[4 * qd + 1]), pack_bf16x2(v[4 * qd + 2], v[4 * qd + 3])};
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int r = r0 + p * RSTEP;  // row in the half
+        const int a = ot_addr(r, c * 8);
+        const u32x4 hv = *reinterpret_cast<const u32x4*>(ot + a);
+        const u32x4 uv = *reinterpret_cast<const u32x4*>(ot + AB + a);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(ot + 2 * AB + a);
+        const int tr = hh * HR + r;  // tile row
+        if (tr < rows_here && col < N0) {
+          *reinterpret_cast<u32x4*>(C + (size_t)(m0 + tr) * N0 + col) = hv;
+          uint16_t* uvrow = UV + (size_t)(m0 + tr) * (2 * N0);
+          *reinterpret_cast<u32x4*>(uvrow + col) = uv;
+          *reinterpret_cast<u32x4*>(uvrow + N0 + col) = vv;
         }
       }
     }
