@@ -26,9 +26,14 @@
  *  - Argument errors are detected on the host before anything is enqueued
  *    and return MOE_ERR_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE with
  *    the outputs untouched. A failed kernel launch returns MOE_ERR_DEVICE.
- *  - Out-of-range VALUES inside device arrays (an expert id outside [0,E), a
- *    rank outside [0,G), NaN logits) cannot be seen by the host and give
- *    unspecified (but in-bounds) results.
+ *  - VALUES inside device arrays cannot be seen by the host. The routing,
+ *    co-activation and layout calls stay in bounds for any values: an expert
+ *    id outside [0,E) or a rank outside [0,G) drops that choice (no slot, no
+ *    row, slot_of -1), a repeated expert within a token or a NaN logit gives
+ *    unspecified results. The expert, combine and backward calls trust the
+ *    index arrays a layout call produced (perm_row, expert_off, slot_of);
+ *    there a negative slot_of entry is a dropped choice that reads and adds
+ *    nothing. moe_validate_routing checks routing inputs on the device.
  *  - Limits: 0 <= T, 1 <= k <= 16, k <= E <= 256, 1 <= G <= 32,
  *    T*k < 2^31. For the expert FFN d and F must be multiples of 64 and the
  *    FFN's tensors 16-byte aligned; in bf16 each call's activation operand
@@ -138,8 +143,8 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, in
  *  rep_mask [E] uint32 (device): bit g set iff rank g holds a copy of expert
  *           e (bits >= G are ignored). Every expert a token chooses should
  *           have a copy: a choice without one is dropped (rank_of -1,
- *           slot_of -1, no slot and no row), and moe_combine must not be
- *           run on such a layout.
+ *           slot_of -1, no slot and no row); the combine and backward
+ *           calls leave it out (it has no expert output).
  *  ranks_per_node: ranks [n*rpn, (n+1)*rpn) form node n; rpn | G.
  * Assignment, per token t (home rank t*G/T, i.e. tokens sharded in order
  * over the ranks; home node = home rank / rpn), over its valid choices:
@@ -229,7 +234,8 @@ moe_status moe_grouped_ffn(const void* x_disp, const int32_t* perm_row, const in
  * results are combined): out[t] = sum_j gates[t,j] * y[slot_of[t*k+j]],
  * accumulated in fp32 in j order, stored in dt (bf16: RNE).
  *  y [T*k,d] (dt), slot_of [T*k], gates [T,k] fp32 (NULL: every gate is
- *  1), out [T,d] (dt) out.
+ *  1), out [T,d] (dt) out. A choice with slot_of < 0 (dropped by
+ *  moe_replica_layout) is left out of the sum and no y row is read for it.
  */
 moe_status moe_combine(const void* y, const int32_t* slot_of, const float* gates,
                        int32_t T, int32_t k, int32_t d, moe_dtype dt, void* out,
@@ -254,7 +260,8 @@ moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t* perm_row,
 
 /* Combine backward: dy[slot_of[t*k+j]] = gates[t,j] * dout[t] (dt) and
  * dgates[t,j] = <dout[t], y[slot_of[t*k+j]]> (fp32 accumulation).
- *  dout [T,d], y [T*k,d], dy [T*k,d] (dt); gates, dgates [T,k] fp32. */
+ *  dout [T,d], y [T*k,d], dy [T*k,d] (dt); gates, dgates [T,k] fp32.
+ *  A dropped choice (slot_of < 0) writes no dy row and gets dgates 0. */
 moe_status moe_combine_bwd(const void* dout, const void* y, const int32_t* slot_of,
                            const float* gates, int32_t T, int32_t k, int32_t d, moe_dtype dt,
                            void* dy, float* dgates, hipStream_t stream);
@@ -290,7 +297,8 @@ moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp, const int
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch backward: dx[t] = sum_j da[slot_of[t*k+j]] (fp32 accumulation in
- * j order, stored in dt). da [T*k,d], dx [T,d]. */
+ * j order, stored in dt) over the choices with slot_of >= 0.
+ * da [T*k,d], dx [T,d]. */
 moe_status moe_dispatch_bwd(const void* da, const int32_t* slot_of, int32_t T, int32_t k,
                             int32_t d, moe_dtype dt, void* dx, hipStream_t stream);
 
@@ -299,6 +307,30 @@ moe_status moe_dispatch_bwd(const void* da, const int32_t* slot_of, int32_t T, i
  *  entry 0. gates, dgates [T,k] fp32, dlogits [T,E] fp32 out. E <= 1024. */
 moe_status moe_route_bwd(const float* gates, const float* dgates, const int32_t* topk_idx,
                          int32_t T, int32_t E, int32_t k, float* dlogits, hipStream_t stream);
+
+/*
+ * Device-side validation of routing inputs, for debugging (the binding runs
+ * it after routing when MOE_DEBUG=1 is set). Each check covers a value the
+ * host cannot see and the other calls do not define:
+ *  logits   [T,E] fp32 (or NULL): a NaN logit has no place in the descending
+ *           order of logits (Zyphra page, English abstract: each token goes
+ *           to k of the E experts)                      -> MOE_BAD_LOGIT;
+ *  topk_idx [T,k] int32 (or NULL): each entry in [0,E)  -> MOE_BAD_EXPERT,
+ *           and the k entries of a token distinct       -> MOE_BAD_REPEAT;
+ *  place    [E] int32 (or NULL): each rank in [0,G)     -> MOE_BAD_RANK.
+ *  err      [1] uint32 in/out: the flags found are OR-ed in; zero it first.
+ * Asynchronous like every call: read err after synchronising the stream.
+ * k <= 16. Nothing traps; the kernel reads every value once.
+ */
+enum {
+    MOE_BAD_LOGIT = 1u,
+    MOE_BAD_EXPERT = 2u,
+    MOE_BAD_REPEAT = 4u,
+    MOE_BAD_RANK = 8u
+};
+moe_status moe_validate_routing(const float* logits, const int32_t* topk_idx, int32_t T,
+                                int32_t E, int32_t k, const int32_t* place, int32_t G,
+                                uint32_t* err, hipStream_t stream);
 
 /*
  * Expert placement planner (host code; every pointer is HOST memory).

@@ -46,7 +46,10 @@ def silu_grad(u):
 # ---------------------------------------------------------------- steps
 
 def combine_bwd(dout, y, slot_of, gates):
-    """-> dy [S, d] (dy[slot(t,j)] = g_tj dout[t]), dgates [T, k]."""
+    """-> dy [S, d] (dy[slot(t,j)] = g_tj dout[t]), dgates [T, k].
+
+    A negative slot is a dropped choice (no expert output in the forward):
+    it writes no dy row and its gate gradient is 0."""
     dout = np.asarray(dout, np.float64)
     y = np.asarray(y, np.float64)
     g = np.asarray(gates, np.float64)
@@ -55,9 +58,10 @@ def combine_bwd(dout, y, slot_of, gates):
     dy = np.zeros_like(y)
     dgates = np.zeros((T, k))
     for j in range(k):
-        s = so[:, j]
-        dy[s] = g[:, j:j + 1] * dout
-        dgates[:, j] = (dout * y[s]).sum(1)
+        live = so[:, j] >= 0
+        s = so[live, j]
+        dy[s] = g[live, j:j + 1] * dout[live]
+        dgates[live, j] = (dout[live] * y[s]).sum(1)
     return dy, dgates
 
 
@@ -108,10 +112,15 @@ def gate_up_bwd(du, dv, a_rows, expert_off, w_gate, w_up):
 
 
 def dispatch_bwd(da, slot_of, T, k):
-    """dx[t] = sum_j da[slot(t, j)]."""
+    """dx[t] = sum_j da[slot(t, j)] over the choices with a slot (a negative
+    slot is a dropped choice and adds nothing)."""
     da = np.asarray(da, np.float64)
     so = np.asarray(slot_of).reshape(T, k)
-    return sum(da[so[:, j]] for j in range(k)) if k else np.zeros((T, da.shape[1]))
+    dx = np.zeros((T, da.shape[1]))
+    for j in range(k):
+        live = so[:, j] >= 0
+        dx[live] += da[so[live, j]]
+    return dx
 
 
 def route_bwd(gates, dgates, topk_idx, E):

@@ -282,20 +282,26 @@ int orc_ffn_rows(const void* x, int dt, int d, int F, int n_rows,
 /*
  * Combine back to token order (Zyphra page, English abstract: the results
  * are combined after the experts). Reading: the gate multiplies the expert
- * output,  out[t] = sum_j gates[t][j] * y[slot_of[t*k+j]].
+ * output,  out[t] = sum_j gates[t][j] * y[slot_of[t*k+j]]. A negative slot
+ * is a choice the replica-aware assignment dropped (Cobalt page, English
+ * abstract: tokens go to expert replicas; a choice whose expert has no copy
+ * has no expert output), so its term is absent.
  */
 int orc_combine(const double* y, int n_slots, const int32_t* slot_of, const double* gates,
                 int T, int k, int d, double* out)
 {
     if (T < 0 || k < 1 || d < 1) return -1;
     for (size_t i = 0; i < (size_t)T * k; ++i)
-        if (slot_of[i] < 0 || slot_of[i] >= n_slots) return -1;
+        if (slot_of[i] >= n_slots) return -1;
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int c = 0; c < d; ++c) {
             double acc = 0.0;
-            for (int j = 0; j < k; ++j)
-                acc += gates[(size_t)t * k + j] * y[(size_t)slot_of[(size_t)t * k + j] * d + c];
+            for (int j = 0; j < k; ++j) {
+                int32_t s = slot_of[(size_t)t * k + j];
+                if (s < 0) continue; /* dropped choice: no expert output */
+                acc += gates[(size_t)t * k + j] * y[(size_t)s * d + c];
+            }
             out[(size_t)t * d + c] = acc;
         }
     }

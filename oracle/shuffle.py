@@ -4,14 +4,13 @@ token-locality statistic.
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use
 this. It shares no code with the library's kernels.
 
-Zyphra correlated expert placement page, English abstract: when sequence
-parallelism shards the tokens over the expert-parallel group, token
-shuffling moves each token, during the reduce-scatter after attention, to
-the GPU predicted to hold its next-layer experts; on one node this raises the
-share of token-expert assignments served on the token's own GPU from 12.5%
-(1/8, what uniform routing gives on 8 GPUs) to 59%. The pages give no rule
-for the prediction or the choice of GPU; the reading implemented (and
-followed by the library) is:
+Source: Zyphra correlated expert placement page, English abstract (token
+shuffling under sequence parallelism; the page reports the on-GPU share of
+assignments going from 12.5% to 59% on one node). Reading: a token should sit
+on the GPU that will serve most of its next-layer experts, and 12.5% is 1/8,
+the share uniform routing gives on 8 GPUs. The pages give no rule for the
+prediction or the choice of GPU; the reading implemented (and followed by
+the library) is:
 
   home rank of token t: t * G // T (tokens sharded in order);
   prediction model: an affinity table aff [E, G] >= 0, aff[e][g] = how

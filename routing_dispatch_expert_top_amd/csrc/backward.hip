@@ -49,13 +49,17 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * (blockDim.x / kWave) + wave;
   if (t >= T) return;
+  // A negative slot is a dropped choice: no y row is read, no dy row is
+  // written, and its gate gradient is 0.
   float dot[KM];
   int sl[KM];
   float gt[KM];
+  bool live[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     dot[j] = 0.f;
     sl[j] = j < k ? slot_of[(size_t)t * k + j] : 0;
+    live[j] = j < k && sl[j] >= 0;
     gt[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
   }
   const u32x4* o = dout + (size_t)t * row_vecs;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      if (j >= k) continue;
+      if (!live[j]) continue;
       const float g = gt[j];
       u32x4 w;
       if (BF16) {
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     if (ok1) ov1 = __builtin_nontemporal_load(o + c1);
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-      if (j < k) {
+      if (live[j]) {
         yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov0;
         yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1) : ov1;
       }

@@ -16,6 +16,8 @@
 //    cell into both mirrored entries of the global matrix.
 #include "moe_internal.h"
 
+#include <atomic>
+
 namespace moe {
 namespace {
 
@@ -155,11 +157,22 @@ __global__ __launch_bounds__(256) void coact_global_kernel(const int32_t* __rest
 // grow as E*T*k (4 bytes each, from L2), the triangle kernel's work as T*k*k.
 constexpr int64_t kRowOwnerMaxWork = int64_t(1) << 26;
 
+// LDS bytes a workgroup may use on the current device, cached per device
+// (the relaxed atomics make concurrent first calls from several host threads
+// safe: each stores the same value).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_lds_limit[kMaxDevices];  // 0: not read yet
+
 int max_lds_per_block() {
   int dev = 0, v = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_lds_limit[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return 0;
+  if (dev >= 0 && dev < kMaxDevices && v > 0) g_lds_limit[dev].store(v, std::memory_order_relaxed);
   return v;
 }
 
@@ -190,9 +203,7 @@ MOE_EXPORT moe_status moe_coact_hist(const int32_t* topk_idx, int32_t T, int32_t
     return launch_status();
   }
   const size_t lds = sizeof(uint32_t) * (size_t)E * (E - 1) / 2;
-  static int lds_limit = -1;
-  if (lds_limit < 0) lds_limit = max_lds_per_block();
-  if (lds <= (size_t)lds_limit) {
+  if (lds <= (size_t)max_lds_per_block()) {
     // about 32k pair updates per workgroup, at most one workgroup per CU
     const int64_t pairs = (int64_t)T * k * (k - 1) / 2;
     int nwg = (int)std::min<int64_t>(256, std::max<int64_t>(1, ceil_div(pairs, 32768)));

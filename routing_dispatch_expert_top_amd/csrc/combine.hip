@@ -1,7 +1,8 @@
 // Gate-weighted combine back into token order (Zyphra correlated expert
 // placement page, English abstract: after the experts, the results are
 // combined). out[t] = sum_j gates[t,j] * y[slot_of[t*k+j]], fp32 accumulation
-// in j order, stored in the activation type.
+// in j order, stored in the activation type; a choice with a negative slot
+// (dropped by the replica-aware layout) contributes nothing.
 //
 // gfx950 mapping: one wavefront per token. The token's k slots and gates are
 // wave-uniform and come in through scalar loads (SGPRs); each lane then
@@ -52,12 +53,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * (blockDim.x / kWave) + wave;  // wave-uniform
   if (t >= T) return;
+  // A negative slot is a dropped choice (no copy of its expert was
+  // assigned): it reads nothing and adds nothing.
   const u32x4* rows[KM];
   float g[KM];
+  bool live[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
+    live[j] = false;
     if (j < k) {
-      rows[j] = y + (size_t)slot_of[(size_t)t * k + j] * row_vecs;
+      const int s = slot_of[(size_t)t * k + j];
+      live[j] = s >= 0;
+      rows[j] = y + (size_t)(live[j] ? s : 0) * row_vecs;
       g[j] = gates ? gates[(size_t)t * k + j] : 1.0f;
     }
   }
@@ -79,14 +86,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     u32x4 v0[KM], v1[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-      if (j < k) {
+      if (j < k && live[j]) {
         v0[j] = ok0 ? __builtin_nontemporal_load(rows[j] + c0) : u32x4{0, 0, 0, 0};
         v1[j] = ok1 ? __builtin_nontemporal_load(rows[j] + c1) : u32x4{0, 0, 0, 0};
       }
     float a0[8] = {}, a1[8] = {};
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-      if (j < k) {
+      if (j < k && live[j]) {
         accum<BF16>(a0, v0[j], g[j]);
         accum<BF16>(a1, v1[j], g[j]);
       }

@@ -69,6 +69,7 @@ def lib():
                                             p, p, p, sz, p]),
             "moe_replica_layout": (C.c_int, [p, i32, i32, i32, p, i32, i32, p, i32, C.c_int,
                                              p, p, p, p, p, p, p, p, p, p, sz, p]),
+            "moe_validate_routing": (C.c_int, [p, p, i32, i32, i32, p, i32, p, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -338,6 +339,33 @@ def moe_route_bwd(gates, dgates, topk_idx, E, dlogits=None, stream=None):
     return dlogits
 
 
+MOE_BAD_LOGIT, MOE_BAD_EXPERT, MOE_BAD_REPEAT, MOE_BAD_RANK = 1, 2, 4, 8
+_BAD_NAMES = {MOE_BAD_LOGIT: "NaN logit", MOE_BAD_EXPERT: "expert id outside [0,E)",
+              MOE_BAD_REPEAT: "expert repeated within a token",
+              MOE_BAD_RANK: "rank outside [0,G)"}
+
+
+def moe_validate_routing(logits, topk_idx, E, place=None, G=1, stream=None):
+    """Device-side check of routing inputs; synchronises the stream and
+    returns the flags found (0: nothing wrong). logits / topk_idx / place may
+    each be None to skip that check."""
+    T, k = topk_idx.shape if topk_idx is not None else (logits.shape[0], 1)
+    ref = next(a for a in (logits, topk_idx, place) if a is not None)
+    err = torch.zeros(1, dtype=torch.int32, device=ref.device)
+    _check("moe_validate_routing", lib().moe_validate_routing(
+        _ptr(logits), _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(err), _stream(stream)))
+    torch.cuda.synchronize(ref.device)  # the kernel may run on another stream than torch's
+    return int(err.cpu().item()) & 0xFFFFFFFF
+
+
+def bad_routing_names(flags: int):
+    return [n for b, n in _BAD_NAMES.items() if flags & b]
+
+
+def debug_enabled() -> bool:
+    return os.environ.get("MOE_DEBUG", "0") not in ("", "0")
+
+
 def moe_plan_placement(coact, load, G, ranks_per_node=1, swap_passes=8):
     """Host call: coact [E,E] and load [E] (array-likes, converted to int64
     host arrays; device tensors are copied to the host first) -> place [E]
@@ -404,9 +432,20 @@ class Layer:
     def combine(self, stream=None):
         moe_combine(self.y, self.lay["slot_of"], self.gates, self.T, self.k, self.out, stream)
 
+    def validate(self, logits, place, stream=None):
+        """MOE_DEBUG: check logits, the routing result and the placement on
+        the device; raise ValueError naming what is wrong."""
+        flags = moe_validate_routing(logits, self.topk_idx, self.E, place, self.G, stream)
+        if flags:
+            raise ValueError("invalid routing inputs: " + ", ".join(bad_routing_names(flags)))
+
     def forward(self, logits, x, place, w_gate, w_up, w_down, stream=None):
-        """One pass of the whole hot path; the co-activation counts accumulate."""
+        """One pass of the whole hot path; the co-activation counts accumulate.
+        With MOE_DEBUG=1 in the environment the routing inputs are validated
+        on the device after routing (this synchronises)."""
         self.route(logits, stream)
+        if debug_enabled():
+            self.validate(logits, place, stream)
         self.coact_hist(stream)
         self.dispatch(x, place, stream)
         self.gate_up(w_gate, w_up, stream)

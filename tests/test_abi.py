@@ -15,7 +15,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = ops.header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
 
@@ -52,6 +52,15 @@ NULL = None
 ])
 def test_route_argument_errors(L, args, want):
     assert L.moe_route(*args) == want
+
+
+def test_validate_argument_errors(L):
+    err = 16  # never dereferenced: every call below fails its argument check
+    assert L.moe_validate_routing(NULL, NULL, -1, 8, 2, NULL, 4, err, NULL) == ops.MOE_ERR_ARG
+    assert L.moe_validate_routing(NULL, NULL, 4, 8, 2, NULL, 4, NULL, NULL) == ops.MOE_ERR_ARG
+    assert L.moe_validate_routing(NULL, NULL, 4, 0, 2, NULL, 4, err, NULL) == ops.MOE_ERR_ARG
+    assert L.moe_validate_routing(NULL, NULL, 4, 64, 17, NULL, 4, err, NULL) == \
+        ops.MOE_ERR_UNSUPPORTED
 
 
 def test_coact_argument_errors(L):

@@ -96,3 +96,30 @@ def test_silu_grad_closed_forms():
     assert B.silu_grad(np.array([0.0]))[0] == 0.5
     u = np.array([-30.0, 30.0])
     assert np.allclose(B.silu_grad(u), [0.0, 1.0], atol=1e-10)
+
+
+def test_dropped_choices_are_zero_rows():
+    """A dropped choice (negative slot) acts as an expert output of zero with
+    weight zero: combine_bwd and dispatch_bwd on it equal the same calls with
+    the choice pointed at an extra all-zero row, which is then removed."""
+    rng = np.random.default_rng(8)
+    T, k, d = 30, 4, 6
+    S = T * k
+    so = rng.permutation(S).astype(np.int32)
+    drop = rng.random(S) < 0.25
+    drop[:k] = True
+    so_d = np.where(drop, -1, so).astype(np.int32)
+    so_z = np.where(drop, S, so).astype(np.int32)        # the extra zero row
+    dout = rng.standard_normal((T, d))
+    y = rng.standard_normal((S, d))
+    gates = rng.random((T, k))
+    y_z = np.vstack([y, np.zeros((1, d))])
+    dy, dg = B.combine_bwd(dout, y, so_d, gates)
+    g_z = np.where(drop.reshape(T, k), 0.0, gates)
+    dy_z, dg_z = B.combine_bwd(dout, y_z, so_z, g_z)
+    assert np.array_equal(dy, dy_z[:S]) and np.array_equal(dg, dg_z)
+    assert not dg[0].any()
+    da = rng.standard_normal((S, d))
+    dx = B.dispatch_bwd(da, so_d, T, k)
+    dx_z = B.dispatch_bwd(np.vstack([da, np.zeros((1, d))]), so_z, T, k)
+    assert np.array_equal(dx, dx_z) and not dx[0].any()

@@ -20,12 +20,15 @@ MUTANTS = [
      "return dh * v * silu_grad(u), dh * silu_grad(u)"),
     ("dgates_no_inner", "g * (dg - inner)", "g * dg"),
     ("dgates_sign", "g * (dg - inner)", "g * (inner - dg)"),
-    ("dy_without_gate", "dy[s] = g[:, j:j + 1] * dout", "dy[s] = dout"),
+    ("dy_without_gate", "dy[s] = g[live, j:j + 1] * dout[live]", "dy[s] = dout[live]"),
     ("da_drops_up", "da[a:b] = du[a:b] @ wg[e] + dv[a:b] @ wu[e]", "da[a:b] = du[a:b] @ wg[e]"),
     ("dw_up_from_du", "dwu[e] = dv[a:b].T @ ar[a:b]", "dwu[e] = du[a:b].T @ ar[a:b]"),
     ("dw_down_uses_u", "dwd[e] = dy[a:b].T @ h[a:b]", "dwd[e] = dy[a:b].T @ np.asarray(u, np.float64)[a:b]"),
-    ("dx_first_choice_only", "return sum(da[so[:, j]] for j in range(k))",
-     "return sum(da[so[:, j]] for j in range(1))"),
+    ("dx_first_choice_only", "dx = np.zeros((T, da.shape[1]))\n    for j in range(k):",
+     "dx = np.zeros((T, da.shape[1]))\n    for j in range(1):"),
+    ("dx_reads_dropped_choices", "dx[live] += da[so[live, j]]", "dx += da[so[:, j]]"),
+    ("dgates_of_dropped_choice", "dgates[live, j] = (dout[live] * y[s]).sum(1)",
+     "dgates[:, j] = (dout * y[so[:, j]]).sum(1)"),
     ("slot_order_token_major", "order = np.lexsort((j_of, t_of, e_of))",
      "order = np.lexsort((j_of, e_of, t_of))"),
 ]
@@ -42,7 +45,8 @@ def _load(name, old, new):
 def _pin_suite():
     cases = [lambda a=a: pins.test_gradients_match_finite_differences(*a) for a in [(0, 2)]]
     cases += [pins.test_forward_recompute_matches_c_oracle, pins.test_softmax_jacobian_invariants,
-              pins.test_unused_expert_gets_zero_weight_gradient, pins.test_silu_grad_closed_forms]
+              pins.test_unused_expert_gets_zero_weight_gradient, pins.test_silu_grad_closed_forms,
+              pins.test_dropped_choices_are_zero_rows]
     failed = 0
     for c in cases:
         try:

@@ -6,7 +6,11 @@ then the whole layer (forward with saved pre-activations, then every
 backward step) against oracle.backward.layer_backward, and at the full
 T=8192, d=4096, E=128, k=8, F=1536 size on sampled experts and tokens that the
 reference evaluates on its own. Tolerance: max|gpu - ref| <= tau * max|ref|
-per tensor, tau = 1e-4 (fp32) and 2e-2 (bf16) as in the forward tests.
+per tensor, tau = 1e-4 (fp32) and 2e-2 (bf16) as in the forward tests. The
+fp32 weight gradients of the step and segment tests, whose inputs the GPU
+reads exactly, are held to 1e-4 per expert; in the whole-layer tests they are
+computed from bf16-rounded intermediates (dy, du, dv, h), so the bf16
+tolerance bounds them there.
 """
 import numpy as np
 import pytest
@@ -34,6 +38,18 @@ def _store(a, dtype):
 
 def _w(a):
     return widen(a) if a.dtype in (np.uint16, np.float32) else np.asarray(a, np.float64)
+
+
+def per_expert_close(name, got, ref, eo):
+    """fp32 weight gradients whose inputs are exact (bf16 or fp32 values the
+    GPU reads as they are): fp32 accumulation error only, so each expert is
+    held to the fp32 tolerance against its own largest reference entry, and
+    an expert without slots must be exactly zero."""
+    for e in range(len(eo) - 1):
+        if eo[e + 1] == eo[e]:
+            assert (got[e] == 0).all(), f"{name}[{e}] of an empty expert is not zero"
+        else:
+            assert_close(f"{name}[{e}]", got[e], ref[e], TAU["f32"])
 
 
 def _ragged_offsets(E, S, rng):
@@ -97,8 +113,7 @@ def test_expert_bwd_steps(T, k, E, d, F, dtype, seed):
     g_duv = host(duv)
     assert_close("du", g_duv[:, :F], rdu, TAU[dtype])
     assert_close("dv", g_duv[:, F:], rdv, TAU[dtype])
-    assert_close("dw_down", host(dwd), rdwd, TAU[dtype])
-    assert (host(dwd)[np.diff(eo) == 0] == 0).all()
+    per_expert_close("dw_down", host(dwd), rdwd, eo)
 
     R = S + 5
     x_disp = _store(rng.standard_normal((R, d)), dtype)
@@ -112,8 +127,8 @@ def test_expert_bwd_steps(T, k, E, d, F, dtype, seed):
     rda, rdwg, rdwu = OB.gate_up_bwd(_w(duv_in)[:, :F], _w(duv_in)[:, F:], _w(x_disp)[perm_row],
                                      eo, _w(wg), _w(wu))
     assert_close("da", host(da), rda, TAU[dtype])
-    assert_close("dw_gate", host(dwg), rdwg, TAU[dtype])
-    assert_close("dw_up", host(dwu), rdwu, TAU[dtype])
+    per_expert_close("dw_gate", host(dwg), rdwg, eo)
+    per_expert_close("dw_up", host(dwu), rdwu, eo)
 
 
 
@@ -144,8 +159,7 @@ def test_expert_bwd_segment_boundaries():
     g_duv = host(duv)
     assert_close("du", g_duv[:, :F], rdu, TAU["bf16"])
     assert_close("dv", g_duv[:, F:], rdv, TAU["bf16"])
-    assert_close("dw_down", host(dwd), rdwd, TAU["bf16"])
-    assert (host(dwd)[np.diff(eo) == 0] == 0).all()
+    per_expert_close("dw_down", host(dwd), rdwd, eo)
 
     R = 3000
     x_disp = bf(rng.standard_normal((R, d)))
@@ -162,15 +176,13 @@ def test_expert_bwd_segment_boundaries():
     rda, rdwg, rdwu = OB.gate_up_bwd(_w(duv_in)[:, :F], _w(duv_in)[:, F:], _w(x_disp)[perm_row],
                                      eo, _w(wg), _w(wu))
     assert_close("da", host(da), rda, TAU["bf16"])
-    assert_close("dw_gate", host(dwg), rdwg, TAU["bf16"])
-    assert_close("dw_up", host(dwu), rdwu, TAU["bf16"])
-    # per expert as well, so a short segment's rows and gradients are not hidden by the others
+    per_expert_close("dw_gate", host(dwg), rdwg, eo)
+    per_expert_close("dw_up", host(dwu), rdwu, eo)
+    # da per expert as well, so a short segment's rows are not hidden by the others
     for e in range(E):
         a, b = eo[e], eo[e + 1]
-        tol = TAU["bf16"]
-        assert np.abs(widen(host(da))[a:b] - rda[a:b]).max(initial=0) <= tol * np.abs(rda).max(), e
-        assert np.abs(host(dwg)[e] - rdwg[e]).max() <= tol * np.abs(rdwg).max(), e
-        assert np.abs(host(dwd)[e] - rdwd[e]).max() <= tol * np.abs(rdwd).max(), e
+        if b > a:
+            assert_close(f"da[{e}]", host(da)[a:b], rda[a:b], TAU["bf16"])
 
 def _gpu_train_step(w, inp, dout, place):
     """Forward (saving u, v) and every backward step on the GPU."""

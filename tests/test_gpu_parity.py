@@ -7,10 +7,12 @@ out 1e-4 in fp32 and 2e-2 in bf16.
 
 Small shapes are checked element by element on every output; they span
 several tiles with ragged tails, empty experts, k = 1, k = E, the largest
-E / k / G, an odd E and an empty batch. The five workload shapes are run at
-full size in the same launch configuration as the benchmark; there the
-integer outputs and the dispatched rows are compared in full, and h, y, out
-on a seeded sample of tokens that the oracle evaluates one by one.
+E / k / G, an odd E, -inf logits and an empty batch. The five workload shapes
+are run at full size in the same launch configuration as the benchmark; there
+the integer outputs and the dispatched rows are compared in full, h, y and
+out in full for the first four, and for the largest (T=16384, d=7168, E=256)
+h and y on one slot of every 32-row band of every expert plus out on a token
+sample, each evaluated by the oracle on its own.
 """
 import numpy as np
 import pytest
@@ -73,6 +75,31 @@ def test_layer_parity_small(w, kind):
     assert_close("out", g["out"], ref["out"], tau)
 
 
+def test_layer_parity_neg_inf_logits():
+    """-inf router logits act as masks (each token keeps at least k finite
+    logits): the masked experts are never chosen and the whole layer still
+    matches the oracle."""
+    w = C("bf16_neg_inf", T=700, d=128, E=16, k=4, F=128, G=4, dtype="bf16", clusters=4)
+    inp = synth.make(w, place="colocated")
+    rng = np.random.default_rng(17)
+    mask = rng.random((w.T, w.E)) < 0.4
+    mask[np.arange(w.T)[:, None], np.argsort(rng.random((w.T, w.E)), 1)[:, :w.k]] = False
+    mask[5] = True
+    mask[5, :w.k] = False                      # exactly k finite logits
+    logits = inp["logits"].copy()
+    logits[mask] = -np.inf
+    inp = dict(inp, logits=logits)
+    ref = oracle.layer(logits, inp["x"], inp["place"], w.G, w.k, inp["w_gate"], inp["w_up"],
+                       inp["w_down"], want_h=True)
+    g = run_layer(w, DevInputs(w, inp))
+    assert not mask[np.arange(w.T)[:, None], g["topk_idx"]].any()
+    compare_exact(g, ref)
+    assert np.array_equal(g["x_disp"], ref["x_disp"])
+    assert_close("gates", g["gates"], ref["gates"], TAU_GATES)
+    for key in ("h", "y", "out"):
+        assert_close(key, g[key], ref[key], TAU["bf16"])
+
+
 def test_empty_batch():
     w = C("empty", T=0, d=64, E=8, k=2, F=64, G=4, dtype="bf16")
     lay = ops.Layer(0, 64, 8, 2, 64, 4, torch.bfloat16, "cuda")
@@ -89,20 +116,23 @@ def test_empty_batch():
 
 
 def test_coact_accumulates_and_repeats_bit_exactly():
+    """Ten passes of the layer on the same inputs: the histogram holds ten
+    times the counts and every other output is bit-identical each time (the
+    race check: no result may depend on the order of atomics or of waves)."""
     w = synth.with_shape(synth.workload(2), T=1024)
     inp = synth.make(w, place="colocated")
     d_in = DevInputs(w, inp)
     dt = torch.bfloat16
     lay = ops.Layer(w.T, w.d, w.E, w.k, w.F, w.G, dt, "cuda")
     outs = []
-    for _ in range(3):
+    for _ in range(10):
         lay.forward(d_in.logits, d_in.x, d_in.place, d_in.w_gate, d_in.w_up, d_in.w_down)
         torch.cuda.synchronize()
         outs.append({k: host(v).copy() for k, v in
                      dict(out=lay.out, y=lay.y, h=lay.h, perm=lay.lay["perm_row"],
                           slot=lay.lay["slot_of"], tok=lay.lay["disp_token"]).items()})
     ref_c = oracle.coact(oracle.route(inp["logits"], w.k)[0], w.E)
-    assert np.array_equal(host(lay.coact).astype(np.int64), 3 * ref_c)
+    assert np.array_equal(host(lay.coact).astype(np.int64), 10 * ref_c)
     for o in outs[1:]:
         for key in o:
             assert np.array_equal(o[key], outs[0][key]), key
@@ -155,7 +185,16 @@ def test_route_group_limited(E, ng, tg, k):
     logits = rng.standard_normal((T, E)).astype(np.float32)
     logits[::3] = np.round(logits[::3] * 2.0) / 2.0
     logits[1::7, 0] = -0.0
+    # -inf masks: in rows 2, 7, 12, ... one expert per group, so every group
+    # keeps a finite maximum and the chosen groups hold at least k finite
+    # logits (tg * (E/ng - 1) >= k for every case listed)
+    gs = E // ng
+    assert tg * (gs - 1) >= k
+    rows = np.arange(2, T, 5)
+    cols = (np.arange(ng)[None, :] * gs + (rows[:, None] % gs))
+    logits[rows[:, None], cols] = -np.inf
     idx_ref, g_ref = oracle.route(logits, k, ng, tg)
+    assert np.isfinite(g_ref).all()
     idx, gates = ops.moe_route(dev(logits), k, ng, tg)
     torch.cuda.synchronize()
     assert np.array_equal(host(idx), idx_ref)
@@ -251,6 +290,51 @@ def sampled_check(w, inp, g, n_tok=48, seed=7):
     assert_close("out(sample)", g["out"][toks], out_ref, tau)
 
 
+def band_sample(expert_off, seed=5, band=32):
+    """One random slot in every 32-slot band of every expert's segment, plus
+    each segment's last slot: every m-tile of any tiling of the segments into
+    whole 32-row bands holds at least one sampled slot."""
+    rng = np.random.default_rng(seed)
+    picks = []
+    for e in range(len(expert_off) - 1):
+        a, b = int(expert_off[e]), int(expert_off[e + 1])
+        for s0 in range(a, b, band):
+            picks.append(rng.integers(s0, min(b, s0 + band)))
+        if b > a:
+            picks.append(b - 1)
+    return np.unique(np.asarray(picks, np.int64))
+
+
+def full_check(w, inp, g, ref_lay):
+    """h and y of every slot and out of every token against the oracle."""
+    x_disp = oracle.dispatch_rows(inp["x"], ref_lay["disp_token"])
+    sexp = oracle.slot_experts(ref_lay["expert_off"])
+    y_ref, h_ref = oracle.ffn_rows(x_disp, ref_lay["perm_row"], sexp, inp["w_gate"],
+                                   inp["w_up"], inp["w_down"], want_h=True)
+    tau = TAU[w.dtype]
+    assert_close("h", g["h"], h_ref, tau)
+    del h_ref
+    assert_close("y", g["y"], y_ref, tau)
+    _, gates = oracle.route(inp["logits"], w.k, w.n_groups, w.topk_groups)
+    out_ref = oracle.combine(y_ref, ref_lay["slot_of"], gates, w.T, w.k)
+    assert_close("out", g["out"], out_ref, tau)
+
+
+def stratified_check(w, inp, g, ref_lay):
+    """h and y of a band-stratified slot sample (every 32-row band of every
+    expert), each slot evaluated by the oracle from its token's row; out of a
+    token sample."""
+    slots = band_sample(ref_lay["expert_off"])
+    tok = ref_lay["disp_token"][ref_lay["perm_row"][slots]]
+    sexp = oracle.slot_experts(ref_lay["expert_off"])[slots]
+    y_ref, h_ref = oracle.ffn_rows(inp["x"], tok, sexp, inp["w_gate"], inp["w_up"],
+                                   inp["w_down"], want_h=True)
+    tau = TAU[w.dtype]
+    assert_close("h(bands)", g["h"][slots], h_ref, tau)
+    assert_close("y(bands)", g["y"][slots], y_ref, tau)
+    sampled_check(w, inp, g)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("wi", [0, 1, 2, 3, 4])
 def test_full_size_parity(wi):
@@ -266,13 +350,11 @@ def test_full_size_parity(wi):
     compare_exact(g, ref)
     assert_close("gates", g["gates"], gates, TAU_GATES)
     assert np.array_equal(g["x_disp"], oracle.dispatch_rows(inp["x"], ref["disp_token"]))
-    if wi == 0:
-        full = oracle.layer(inp["logits"], inp["x"], inp["place"], w.G, w.k, inp["w_gate"],
-                            inp["w_up"], inp["w_down"], want_h=True)
-        for key in ("h", "y", "out"):
-            assert_close(key, g[key], full[key], TAU[w.dtype])
+    if wi <= 3:
+        print(f"oracle over all {w.T * w.k} slots", flush=True)
+        full_check(w, inp, g, ref)
     else:
-        sampled_check(w, inp, g)
+        stratified_check(w, inp, g, ref)
 
 
 @pytest.mark.timeout(300)

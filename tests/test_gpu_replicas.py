@@ -161,3 +161,60 @@ def test_full_size_replicas():
     r = reference(idx, w.E, reps, w.G, 8)
     check(g, r)
     assert np.array_equal(g["x_disp"], oracle.dispatch_rows(inp["x"], r["disp_token"]))
+
+
+def test_dropped_choices_downstream():
+    """Combine, combine backward and dispatch backward on a layout with
+    dropped choices (experts without a copy): a dropped choice reads no row,
+    writes no row and adds nothing. The y, dy and da rows sit between NaN
+    guard rows, which must come back untouched."""
+    from oracle import backward as OB
+    from tests.gpu_helpers import TAU, assert_close, widen
+    T, E, k, G, rpn, d = 600, 16, 4, 8, 2, 192
+    idx = _topk(T, E, k, 31)
+    reps = synth.replicas(np.arange(E, dtype=np.int32) % G, G, rpn, 2, 32)
+    reps[1] = []
+    reps[9] = []
+    lay = ops.moe_replica_layout(dev(idx), E, dev(synth.replica_masks(reps).view(np.int32)), G,
+                                 rpn)
+    torch.cuda.synchronize()
+    slot_of = host(lay["slot_of"])
+    S = int(lay["expert_off"][E].item())
+    drop = slot_of < 0
+    assert drop.any() and S == int((~drop).sum())
+    rng = np.random.default_rng(33)
+    bf = lambda a: synth.f32_to_bf16_bits(np.asarray(a, np.float32))
+    gates = rng.random((T, k)).astype(np.float32)
+    nan = float("nan")
+
+    def guarded(rows):
+        """Device buffer: 4 NaN rows, the rows, 4 NaN rows; returns (buffer, view)."""
+        buf = torch.full((S + 8, d), nan, dtype=torch.bfloat16, device="cuda")
+        if rows is not None:
+            buf[4:4 + S] = dev(rows)
+        return buf, buf[4:4 + S]
+
+    def guards_intact(buf):
+        g = torch.cat([buf[:4], buf[4 + S:]]).float()
+        return bool(torch.isnan(g).all().item())
+
+    y = bf(rng.standard_normal((S, d)))
+    ybuf, yv = guarded(y)
+    out = ops.moe_combine(yv, lay["slot_of"], dev(gates), T, k)
+    dout = bf(rng.standard_normal((T, d)))
+    dybuf, dyv = guarded(None)
+    dyv.fill_(7.0)
+    dy, dg = ops.moe_combine_bwd(dev(dout), yv, lay["slot_of"], dev(gates), T, k, dy=dyv)
+    da = bf(rng.standard_normal((S, d)))
+    dabuf, dav = guarded(da)
+    dx = ops.moe_dispatch_bwd(dav, lay["slot_of"], T, k)
+    torch.cuda.synchronize()
+    g64 = gates.astype(np.float64)
+    assert_close("out", host(out), oracle.combine(widen(y), slot_of, g64, T, k), TAU["bf16"])
+    ref_dy, ref_dg = OB.combine_bwd(widen(dout), widen(y), slot_of, gates)
+    assert_close("dy", host(dy), ref_dy, TAU["bf16"])
+    assert_close("dgates", host(dg), ref_dg, 1e-4)
+    assert (host(dg).reshape(-1)[drop] == 0).all()
+    assert_close("dx", host(dx), OB.dispatch_bwd(widen(da), slot_of, T, k), TAU["bf16"])
+    for name, buf in (("y", ybuf), ("dy", dybuf), ("da", dabuf)):
+        assert guards_intact(buf), name

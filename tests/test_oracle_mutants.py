@@ -39,6 +39,7 @@ MUTANTS = [
     ("combine_ignores_gate", "acc += gates[(size_t)t * k + j] * y[", "acc += 1.0 * y["),
     ("combine_first_gate_only", "acc += gates[(size_t)t * k + j] * y[", "acc += gates[(size_t)t * k] * y["),
     ("bf16_widen_wrong_shift", "<< 16;\n    float f;", "<< 15;\n    float f;"),
+    ("combine_dropped_reads_slot0", "if (s < 0) continue;", "if (s < 0) s = 0;"),
 ]
 
 
@@ -56,6 +57,7 @@ def _pin_suite(orc):
               lambda: pins.test_ffn_vs_matmul(orc, "f32"),
               lambda: pins.test_ffn_vs_matmul(orc, "bf16"),
               lambda: pins.test_combine_k1_is_permutation(orc),
+              lambda: pins.test_combine_dropped_choice_is_a_zero_term(orc),
               lambda: pins.test_layer_k_equals_E_is_dense_mixture(orc),
               lambda: pins.test_layer_vs_numpy_pipeline(orc, "f32")]
     failed = 0

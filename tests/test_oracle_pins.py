@@ -321,6 +321,28 @@ def test_combine_k1_is_permutation(orc):
     assert np.array_equal(out, y[so])
 
 
+def test_combine_dropped_choice_is_a_zero_term(orc):
+    """A dropped choice (negative slot: its expert has no copy, so there is no
+    expert output) adds nothing: the same as pointing it at any slot with a
+    zero gate, and a token whose choices are all dropped gets exactly 0."""
+    rng = np.random.default_rng(5)
+    T, k, d = 40, 3, 9
+    S = T * k
+    y = rng.standard_normal((S, d))
+    so = rng.permutation(S).astype(np.int32)
+    g = rng.random((T, k))
+    drop = rng.random(T * k) < 0.3
+    drop[:k] = True                                     # token 0: every choice dropped
+    so_d = np.where(drop, -1, so).astype(np.int32)
+    got = orc.combine(y, so_d, g, T, k)
+    g0 = np.where(drop.reshape(T, k), 0.0, g)
+    want = orc.combine(y, np.where(drop, 0, so).astype(np.int32), g0, T, k)
+    assert np.array_equal(got, want)
+    assert not got[0].any()
+    with pytest.raises(ValueError):
+        orc.combine(y, np.full(T * k, S, np.int32), g, T, k)   # past the last slot
+
+
 def test_layer_k_equals_E_is_dense_mixture(orc):
     w = synth.custom(T=24, d=32, E=4, k=4, F=40, G=2, dtype="f32")
     inp = synth.make(w)

@@ -1,10 +1,10 @@
 """Pins of the reference token shuffling and locality statistic
 (oracle/shuffle.py).
 
-Zyphra correlated expert placement page, English abstract: token shuffling
-moves each token to the GPU predicted to hold its next-layer experts, which
-raises the share of assignments served on the token's GPU above the 1/G of
-uniform routing (12.5% on 8 GPUs). Pinned by
+Source: Zyphra correlated expert placement page, English abstract (token
+shuffling; the page reports the on-GPU share 12.5% -> 59% on one node). The
+reading: a token should sit where most of its next-layer experts are served,
+which beats the 1/G share of uniform routing (12.5% on 8 GPUs). Pinned by
 
 * the hand-worked examples in tests/golden/token_shuffle_worked_example.txt
   (both tie rules, the lowest-rank fallback, a one-hot and a general
