@@ -133,6 +133,28 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, in
                                hipStream_t stream);
 
 /*
+ * moe_dispatch_layout without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation). Same arguments, outputs and orders as
+ * moe_dispatch_layout. Its scratch is a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU (held from the first call on that GPU
+ * until the process ends); the call allocates nothing. Returns
+ * MOE_ERR_WORKSPACE, enqueuing nothing, when the scratch the shape needs
+ * (moe_dispatch_workspace_bytes(T, E, k, G)) exceeds that size; e.g.
+ * T = 16384, E = 256, G = 32 needs 1.3 MB. Every call on a GPU shares that
+ * GPU's scratch: calls that may overlap in time on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                                       const int32_t* place, int32_t G,
+                                       const void* x, int32_t d, moe_dtype dt,
+                                       uint32_t* rank_mask, int32_t* rank_off,
+                                       int32_t* disp_token, int32_t* expert_off,
+                                       int32_t* perm_row, int32_t* slot_of, void* x_disp,
+                                       hipStream_t stream);
+
+/*
  * Replica-aware dispatch layout (Cobalt page, English abstract: expert
  * replicas on GPUs of several nodes, and a communication-aware assignment
  * that routes each token to fewer remote nodes for the current layout).

@@ -27,6 +27,8 @@
 //           row once and writes it to each of its rows (16 bytes per lane).
 #include "moe_internal.h"
 
+#include <atomic>
+
 namespace moe {
 namespace {
 
@@ -470,6 +472,57 @@ MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, in
   return layout_impl(topk_idx, T, E, k, place, nullptr, G, x, d, dt, rank_mask, rank_off,
                      disp_token, expert_off, perm_row, slot_of, x_disp, workspace,
                      workspace_bytes, stream);
+}
+
+namespace moe {
+namespace {
+
+// Scratch of moe_dispatch_layout_noalloc: the layout workspace (per-block key
+// counts, bitmaps and their word prefixes) in a file-scope device array, so
+// that call allocates nothing. Each device holds its own copy at its own
+// address until the process ends; host code uses the address
+// hipGetSymbolAddress returns on that device, never the array's name (a
+// host-side stand-in). Every call writes all of the scratch it later reads,
+// so nothing in it has to start at zero.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static_assert(kNoAllocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "header and library agree");
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up once per
+// device), or nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);  // racing threads store the same value
+  return p;
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_EXPORT moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int32_t T, int32_t E,
+                                                  int32_t k, const int32_t* place, int32_t G,
+                                                  const void* x, int32_t d, moe_dtype dt,
+                                                  uint32_t* rank_mask, int32_t* rank_off,
+                                                  int32_t* disp_token, int32_t* expert_off,
+                                                  int32_t* perm_row, int32_t* slot_of,
+                                                  void* x_disp, hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || G < 1) return MOE_ERR_ARG;
+  if (E > kMaxE || k > kMaxK || G > kMaxG || (int64_t)T * k >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (!place) return MOE_ERR_ARG;
+  if (workspace_layout(T, E, k, G).total > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_DEVICE;
+  return layout_impl(topk_idx, T, E, k, place, nullptr, G, x, d, dt, rank_mask, rank_off,
+                     disp_token, expert_off, perm_row, slot_of, x_disp, ws, kNoAllocScratchBytes,
+                     stream);
 }
 
 MOE_EXPORT moe_status moe_replica_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,

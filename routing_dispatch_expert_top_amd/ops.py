@@ -70,6 +70,8 @@ def lib():
             "moe_replica_layout": (C.c_int, [p, i32, i32, i32, p, i32, i32, p, i32, C.c_int,
                                              p, p, p, p, p, p, p, p, p, p, sz, p]),
             "moe_validate_routing": (C.c_int, [p, p, i32, i32, i32, p, i32, p, p]),
+            "moe_dispatch_layout_noalloc": (C.c_int, [p, i32, i32, i32, p, i32, p, i32,
+                                                      C.c_int, p, p, p, p, p, p, p, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -176,6 +178,22 @@ def moe_dispatch_layout(topk_idx, E, place, G, x=None, out=None, stream=None):
         _ptr(out["expert_off"]), _ptr(out["perm_row"]), _ptr(out["slot_of"]),
         _ptr(out.get("x_disp")) if x is not None else None, _ptr(ws), ws.numel(),
         _stream(stream)))
+    return out
+
+
+def moe_dispatch_layout_noalloc(topk_idx, E, place, G, x=None, out=None, stream=None):
+    """moe_dispatch_layout on the library's own scratch (no workspace); with
+    `out` given (a dict of alloc_layout's buffers) nothing is allocated."""
+    T, k = topk_idx.shape
+    d = x.shape[1] if x is not None else None
+    if out is None:
+        out = alloc_layout(T, E, k, G, topk_idx.device, d, x.dtype if x is not None else None)
+    dt = dtype_code(x) if x is not None else MOE_F32
+    _check("moe_dispatch_layout_noalloc", lib().moe_dispatch_layout_noalloc(
+        _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(x), d or 0, dt,
+        _ptr(out["rank_mask"]), _ptr(out["rank_off"]), _ptr(out["disp_token"]),
+        _ptr(out["expert_off"]), _ptr(out["perm_row"]), _ptr(out["slot_of"]),
+        _ptr(out.get("x_disp")) if x is not None else None, _stream(stream)))
     return out
 
 
