@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -223,6 +223,10 @@ moe_status moe_token_shuffle(const int32_t* want_idx, int32_t T, int32_t E, int3
                              int32_t* pos, void* x_shuf, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Bytes of device workspace the forward expert calls need (host call, no
+ * GPU): the tile queue of their persistent launches. */
+size_t moe_expert_workspace_bytes(void);
+
 /*
  * Expert networks, first half: for every slot s of expert e (expert_off),
  *   a = x_disp[perm_row[s]],  u = W_gate[e] a,  v = W_up[e] a,
@@ -230,26 +234,36 @@ moe_status moe_token_shuffle(const int32_t* want_idx, int32_t T, int32_t E, int3
  * The pages only say "expert networks"; this is a bias-free SwiGLU MLP.
  *  x_disp [*,d] (dt), w_gate / w_up [E,F,d] (dt, output index first),
  *  h [T*k,F] (dt) out; rows expert_off[E]..T*k-1 are not written.
+ *  workspace: at least moe_expert_workspace_bytes() bytes, 16-byte aligned,
+ *  ZERO-FILLED before its first use; every call leaves it zero-filled again
+ *  (it holds the tile queue of the persistent launch, which the launch's
+ *  last workgroup resets). Calls that may run at the same time (other
+ *  streams) need separate workspaces. Missing or small: MOE_ERR_WORKSPACE.
  * bf16: bf16 MFMA with fp32 accumulation, h rounded to bf16 (RNE).
  */
 moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm_row,
                               const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
                               int32_t d, int32_t F, const void* w_gate, const void* w_up,
-                              moe_dtype dt, void* h, hipStream_t stream);
+                              moe_dtype dt, void* h, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * Expert networks, second half: y[s] = W_down[e] h[s] for every slot s of
  * expert e.  h [T*k,F] (dt), w_down [E,d,F] (dt), y [T*k,d] (dt) out.
+ * workspace as for moe_expert_gate_up.
  */
 moe_status moe_expert_down(const void* h, const int32_t* expert_off, int32_t T, int32_t E,
                            int32_t k, int32_t d, int32_t F, const void* w_down, moe_dtype dt,
-                           void* y, hipStream_t stream);
+                           void* y, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Both halves in order: moe_expert_gate_up then moe_expert_down. */
+/* Both halves in order: moe_expert_gate_up then moe_expert_down (one
+ * workspace serves both: the second launch starts after the first has
+ * reset it). */
 moe_status moe_grouped_ffn(const void* x_disp, const int32_t* perm_row, const int32_t* expert_off,
                            int32_t T, int32_t E, int32_t k, int32_t d, int32_t F,
                            const void* w_gate, const void* w_up, const void* w_down, moe_dtype dt,
-                           void* h, void* y, hipStream_t stream);
+                           void* h, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * Combine back to token order (Zyphra page, English abstract: the expert

@@ -37,9 +37,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+# Per-source flags. ffn.hip: the persistent GEMM claims tiles with a
+# single-lane atomic whose result is read only a whole tile later; the
+# atomic optimizer would rewrite it into a wave-wide form that waits for the
+# result (and every load issued before it) right away.
+FILE_FLAGS = {"ffn.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that noise
     noise = "'-packed-fp32-ops' is not a recognized feature"

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   // step, all of their loads issued before any is used.
   const int nblk = (row_vecs + kWave - 1) / kWave;
   const int sb = t % nblk;
-  auto block = [&](int c, const u32x4& ov, const u32x4 (&yv)[KM]) {
+  auto block = [&](auto chk_c, int c, const u32x4& ov, const u32x4 (&yv)[KM]) {
+    constexpr bool CHK = decltype(chk_c)::value;
     float of[8];
     if (BF16) {
 #pragma unroll
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      if (!live[j]) continue;
+      if (j >= k || (CHK && !live[j])) continue;
       const float g = gt[j];
       u32x4 w;
       if (BF16) {
@@ -103,25 +104,36 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       dy[(size_t)sl[j] * row_vecs + c] = w;
     }
   };
-  for (int b = 0; b < nblk; b += 2) {
-    const int p0 = b + sb < nblk ? b + sb : b + sb - nblk;
-    const int p1 = b + 1 + sb < nblk ? b + 1 + sb : b + 1 + sb - nblk;
-    const int c0 = p0 * kWave + lane;
-    const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
-    const bool ok0 = c0 < row_vecs, ok1 = c1 < row_vecs;  // the last block may be partial
-    u32x4 ov0 = {0, 0, 0, 0}, ov1 = {0, 0, 0, 0};
-    u32x4 yv0[KM], yv1[KM];
-    if (ok0) ov0 = __builtin_nontemporal_load(o + c0);
-    if (ok1) ov1 = __builtin_nontemporal_load(o + c1);
+  // CHK: some choice of this token is dropped (rare); the common path has no
+  // per-choice test in its loop
+  auto walk = [&](auto chk_c) {
+    constexpr bool CHK = decltype(chk_c)::value;
+    for (int b = 0; b < nblk; b += 2) {
+      const int p0 = b + sb < nblk ? b + sb : b + sb - nblk;
+      const int p1 = b + 1 + sb < nblk ? b + 1 + sb : b + 1 + sb - nblk;
+      const int c0 = p0 * kWave + lane;
+      const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
+      const bool ok0 = c0 < row_vecs, ok1 = c1 < row_vecs;  // the last block may be partial
+      u32x4 ov0 = {0, 0, 0, 0}, ov1 = {0, 0, 0, 0};
+      u32x4 yv0[KM], yv1[KM];
+      if (ok0) ov0 = __builtin_nontemporal_load(o + c0);
+      if (ok1) ov1 = __builtin_nontemporal_load(o + c1);
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (live[j]) {
-        yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov0;
-        yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1) : ov1;
-      }
-    if (ok0) block(c0, ov0, yv0);
-    if (ok1) block(c1, ov1, yv1);
-  }
+      for (int j = 0; j < KM; ++j)
+        if (j < k && (!CHK || live[j])) {
+          yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov0;
+          yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1) : ov1;
+        }
+      if (ok0) block(chk_c, c0, ov0, yv0);
+      if (ok1) block(chk_c, c1, ov1, yv1);
+    }
+  };
+  bool all_live = true;
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k) all_live = all_live && live[j];
+  if (all_live) walk(std::false_type{});
+  else walk(std::true_type{});
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     if (j >= k) continue;

@@ -76,30 +76,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   // same HBM channels (a fixed start measured ~6% slower).
   const int nblk = (row_vecs + kWave - 1) / kWave;
   const int sb = t % nblk;
-  for (int b = 0; b < nblk; b += 2) {
-    int p0 = b + sb, p1 = b + 1 + sb;
-    if (p0 >= nblk) p0 -= nblk;
-    if (p1 >= nblk) p1 -= nblk;
-    const int c0 = p0 * kWave + lane;
-    const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
-    const bool ok0 = WHOLE || c0 < row_vecs, ok1 = (WHOLE && b + 1 < nblk) || c1 < row_vecs;
-    u32x4 v0[KM], v1[KM];
+  // CHK: some choice of this token is dropped (rare); the common path has no
+  // per-choice test in its loop
+  auto walk = [&](auto chk_c) {
+    constexpr bool CHK = decltype(chk_c)::value;
+    for (int b = 0; b < nblk; b += 2) {
+      int p0 = b + sb, p1 = b + 1 + sb;
+      if (p0 >= nblk) p0 -= nblk;
+      if (p1 >= nblk) p1 -= nblk;
+      const int c0 = p0 * kWave + lane;
+      const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
+      const bool ok0 = WHOLE || c0 < row_vecs, ok1 = (WHOLE && b + 1 < nblk) || c1 < row_vecs;
+      u32x4 v0[KM], v1[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < k && live[j]) {
-        v0[j] = ok0 ? __builtin_nontemporal_load(rows[j] + c0) : u32x4{0, 0, 0, 0};
-        v1[j] = ok1 ? __builtin_nontemporal_load(rows[j] + c1) : u32x4{0, 0, 0, 0};
-      }
-    float a0[8] = {}, a1[8] = {};
+      for (int j = 0; j < KM; ++j)
+        if (j < k && (!CHK || live[j])) {
+          v0[j] = ok0 ? __builtin_nontemporal_load(rows[j] + c0) : u32x4{0, 0, 0, 0};
+          v1[j] = ok1 ? __builtin_nontemporal_load(rows[j] + c1) : u32x4{0, 0, 0, 0};
+        }
+      float a0[8] = {}, a1[8] = {};
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < k && live[j]) {
-        accum<BF16>(a0, v0[j], g[j]);
-        accum<BF16>(a1, v1[j], g[j]);
-      }
-    if (ok0) o[c0] = pack<BF16>(a0);
-    if (ok1) o[c1] = pack<BF16>(a1);
-  }
+      for (int j = 0; j < KM; ++j)
+        if (j < k && (!CHK || live[j])) {
+          accum<BF16>(a0, v0[j], g[j]);
+          accum<BF16>(a1, v1[j], g[j]);
+        }
+      if (ok0) o[c0] = pack<BF16>(a0);
+      if (ok1) o[c1] = pack<BF16>(a1);
+    }
+  };
+  bool all_live = true;
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k) all_live = all_live && live[j];
+  if (all_live) walk(std::false_type{});
+  else walk(std::true_type{});
 }
 
 template <bool BF16, bool WHOLE>

@@ -25,6 +25,8 @@
 #include "moe_internal.h"
 #include "gemm_common.h"
 
+#include <atomic>
+
 namespace moe {
 namespace {
 
@@ -750,6 +752,556 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- persistent forward GEMM
+//
+// The forward gate/up and down launches as a persistent grid: one workgroup
+// per CU (the ring fills a CU's LDS), each walking tiles until its XCD's
+// share is done. What a one-tile workgroup pays per tile (start, tile
+// selection, the activation-row gather's index loads, the first slices'
+// load latency, the output stores' drain) then overlaps the previous tile:
+//  - the tile list is decoded from a per-wave register copy of the expert
+//    schedule (lane l holds experts 4l .. 4l+3), built once;
+//  - tile i+1's activation-row indices are loaded while tile i multiplies;
+//  - tile i+1's first A slice and first two B slices are issued at the start
+//    of tile i's epilogue, into the ring stages tile i's last slices did not
+//    use, while its output is staged through the other two and stored;
+//  - the stores drain while tile i+1 multiplies.
+// Tiles are handed out in order, per XCD: XCD x owns logical tiles
+// [x q, (x+1) q) (the order of decode_tile, q = ceil(tiles / 8)); its
+// workgroups take local tiles s and s + S first (S workgroups per XCD, slot
+// s), then claim the next one from the XCD's counter. Tiles running at one
+// moment on an XCD therefore stay a window of neighbouring tiles that share
+// weight panels and activation tiles in that XCD's L2 (a static walk lets
+// workgroups drift apart and lose that sharing). A claim is made two tiles
+// ahead (in tile i's epilogue, for tile i+2) and handed to the workgroup's
+// other waves through the freed staging area, because the ring leaves no LDS
+// free.
+// The queue (8 counters and a finished-workgroup count) must be zero when a
+// launch starts; the last workgroup to finish sets it back to zero.
+constexpr int kQueueWords = 16;  // 8 XCD counters, the finish count, padding
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void ffn_persistent_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
+    const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
+    uint32_t* __restrict__ queue) {
+  constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, NSA = 2, NSB = 3;
+  using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
+  constexpr int NW = WM * WN;
+  constexpr int CH = BK / 8;
+  constexpr int RPI = 512 / BK;
+  constexpr int A_INS = BM / RPI / NW;
+  constexpr int B_INS = BN / RPI / NW;
+  constexpr int LPS = A_INS + B_INS;
+  constexpr int kStageA = BM * CH, kStageB = BN * CH;  // 16-byte units
+  // output stores per thread and staging pass (a pass is 32 KiB x 2 of rows)
+  constexpr int kStPass = 2 * 32768 / 16 / (WM * WN * kWave);
+  constexpr int kMaxPendSt = (SWIGLU ? 1 : 2) * kStPass;
+  __shared__ u32x4 ring[NSA * kStageA + NSB * kStageB];
+  auto stA = [&](int s) { return ring + (s % NSA) * kStageA; };
+  auto stB = [&](int s) { return ring + NSA * kStageA + (s % NSB) * kStageB; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
+  const int KT = K / BK;
+  const uint32_t krow = (uint32_t)K * 2;
+
+  // ---- expert schedule in registers: lane l holds the m-tile prefix of
+  // experts 4l .. 4l+3 (two values per lane); the decode finds the lane by
+  // a ballot and the expert inside it from scalar loads of expert_off
+  int lane_mt = 0;
+  {
+    int prev = expert_off[min(4 * lane, E)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      const int hi = expert_off[min(e + 1, E)];
+      lane_mt += e < E ? (hi - prev + BM - 1) / BM : 0;
+      prev = hi;
+    }
+  }
+  int incl = lane_mt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  const int excl = incl - lane_mt;
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1) * NT;
+
+  const int xcd = blockIdx.x % kXcd;
+  const int S = gridDim.x / kXcd;  // workgroups per XCD (the grid is a multiple of 8)
+  const int q = (total + kXcd - 1) / kXcd;
+  const int qx = min(q, total - xcd * q);  // tiles of this XCD (may be <= 0)
+
+  // local tile j of this XCD -> expert, n-tile, m-tile, segment (all uniform)
+  struct Tile {
+    int e, nt, mt, seg0, seg1;
+  };
+  auto decode = [&](int j) {
+    const int n = xcd * q + j;
+    const uint64_t bal = __ballot(incl * NT > n);
+    const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)bal) - 1);
+    int first = __builtin_amdgcn_readlane(excl, L);
+    Tile t{0, 0, 0, 0, 0};
+    int lo = expert_off[min(4 * L, E)];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int e = 4 * L + qq;
+      const int hi = expert_off[min(e + 1, E)];
+      const int m = e < E ? (hi - lo + BM - 1) / BM : 0;
+      if (m > 0 && first * NT <= n && n < (first + m) * NT) {
+        t.e = e;
+        const int rem = n - first * NT;
+        const int b = rem / (kMBlock * NT);
+        const int bm = min(kMBlock, m - b * kMBlock);
+        const int within = rem - b * kMBlock * NT;
+        t.nt = within / bm;
+        t.mt = b * kMBlock + within % bm;
+        t.seg0 = lo;
+        t.seg1 = hi;
+      }
+      first += m;
+      lo = hi;
+    }
+    return t;
+  };
+
+  // Lane-dependent values of the tile set-up and the epilogue are derived
+  // from this copy of the thread id, which the compiler cannot see through:
+  // it recomputes them where they are used instead of hoisting them out of
+  // the tile loop and keeping them live across the K loop.
+  auto opaque_tid = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return t;
+  };
+  // the same for uniform values (e.g. the row strides of the output stores)
+  auto opaque_s = [&](int v) {
+    asm volatile("" : "+s"(v));
+    return v;
+  };
+
+  // ---- per-tile geometry
+  // An expert's rows are split evenly, in whole 32-row bands, over its
+  // ceil(rows / BM) m-tiles, so the m-tiles of one weight panel cost the
+  // same and stay in step.
+  auto tile_rows = [&](const Tile& t, int& m0, int& m1) {
+    const int me = t.seg1 - t.seg0, nmt = (me + BM - 1) / BM;
+    const int rows_per = min(BM, ((me + nmt - 1) / nmt + 31) & ~31);
+    m0 = t.seg0 + t.mt * rows_per;
+    m1 = min(t.seg1, m0 + rows_per);
+  };
+  // A wave's DMA slots fetch tile rows 64 wave .. 64 wave + 63 (slot i of
+  // lane l: row 64 wave + 8 i + l / 8). Each lane loads the perm_row entry
+  // of row 64 wave + l (gate/up gathers its rows; down reads h in slot
+  // order), and set_aoff hands the entries to the slots by lane shuffles.
+  auto load_rows = [&](int m0, int m1) {
+    const int ln = opaque_tid() & (kWave - 1);
+    const int sl = min(m0 + 64 * wave + ln, m1 - 1);
+    return SWIGLU ? perm_row[sl] : sl;
+  };
+  uint32_t aoff[A_INS], boff[B_INS];
+  auto set_aoff = [&](int src_row) {
+    const int ln = opaque_tid() & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = RPI * (wave * A_INS + i) + ln / CH;
+      const int c = swz_ch<CH>(r, ln % CH) - r * CH;
+      const int src = __shfl(src_row, RPI * i + ln / CH, kWave);
+      aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
+    }
+  };
+  const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
+  auto set_boff = [&](int c0) {
+    const int ln = opaque_tid() & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int r = RPI * (wave * B_INS + i) + ln / CH;
+      const int c = swz_ch<CH>(r, ln % CH) - r * CH;
+      const int n = min(c0 + (b_up ? r - BN / 2 : r), N0 - 1);
+      boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
+    }
+  };
+  const char* a_base = reinterpret_cast<const char*>(A) - kDmaBias;
+  auto b_base_of = [&](int e) {
+    return reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow - kDmaBias;
+  };
+  // DMA instructions i, i+1 (i even) of K slice kt into ring slot gs
+  // (slots count slices across tiles: slice kt of a tile starting at slot g
+  // goes to stA(g + kt), stB(g + kt))
+  auto dma2 = [&](int i, int kt, int gs, const char* b_base) {
+    const bool is_a = i < A_INS;
+    const int ii = is_a ? i : i - A_INS;
+    const int ins = is_a ? A_INS : B_INS;
+    const u32x4* stage = is_a ? stA(gs) : stB(gs);
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        lds_addr(stage + RPI * (wave * ins + (ii & ~3)) * CH));
+    const char* base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
+    const uint32_t v0 = is_a ? aoff[ii] : boff[ii];
+    const uint32_t v1 = is_a ? aoff[ii + 1] : boff[ii + 1];
+    if ((ii & 3) == 0) dma_pair<0>(v0, v1, base, m0v);
+    else dma_pair<2048>(v0, v1, base, m0v);
+  };
+  // first A slice and first NSB-1 B slices of a tile starting at slot g
+  auto prologue = [&](int g, const char* b_base) {
+#pragma unroll
+    for (int p = 0; p < NSA - 1; ++p)
+      if (p < KT) {
+#pragma unroll
+        for (int i = 0; i < A_INS; i += 2) dma2(i, p, g + p, b_base);
+      }
+#pragma unroll
+    for (int p = 0; p < NSB - 1; ++p)
+      if (p < KT) {
+#pragma unroll
+        for (int i = A_INS; i < LPS; i += 2) dma2(i, p, g + p, b_base);
+      }
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  auto band_row = [&](int tm) { return (tm * WM + wm) * 32; };
+  const int li = lane & 31, lk = lane >> 5;
+  // Fragment addresses. Fragment rows are r = 32 b + li (b: a 32-row band),
+  // so the swizzle term (r / 2) & 7 = (li / 2) & 7 is the same for every
+  // fragment of a lane: the LDS index of (row r, chunk c) splits into a
+  // per-lane part li CH + (c ^ xo), one value per k-step, a wave-uniform part
+  // and a compile-time band offset that the LDS read takes as an immediate.
+  // (Left to itself the compiler keeps one address per fragment and k-step
+  // live, which crowds out the tile loop's own registers.)
+  const int xo = (li >> 1) & 7;
+  const int a_uni = wm * 32 * CH;  // band_row(tm) CH = a_uni + tm WM 32 CH
+  auto b_row0 = [&](int tn) {        // first B row of fragment tn
+    if (SWIGLU) {
+      constexpr int half = Cfg::TN / 2;
+      return (tn < half ? 0 : BN / 2) + wn * (Cfg::kWaveCols / 2) + (tn % half) * 32;
+    }
+    return wn * Cfg::kWaveCols + tn * 32;
+  };
+  auto lane_off = [&](int ks) { return li * CH + ((2 * ks + lk) ^ xo); };
+
+  // ---- the walk
+  int cur_j = blockIdx.x / kXcd;  // slot s: local tiles s, s + S, then claims
+  int nxt_j = cur_j + S;
+  Tile cur{}, nxt{};
+  int cm0 = 0, cm1 = 0, nm0 = 0, nm1 = 0;
+  int nsrc = 0;
+  int g = 0;  // ring slot of the current tile's slice 0
+  const char* b_base = nullptr;
+  if (cur_j < qx) {
+    cur = decode(cur_j);
+    tile_rows(cur, cm0, cm1);
+    set_aoff(load_rows(cm0, cm1));
+    set_boff(cur.nt * Cfg::kOutCols);
+    b_base = b_base_of(cur.e);
+    prologue(0, b_base);
+  }
+  int pend_st = 0;  // store instructions of the previous epilogue (per thread, uniform)
+  while (cur_j < qx) {
+    const bool has_next = nxt_j < qx;  // uniform
+    int claim = 0;
+    if (has_next) {
+      nxt = decode(nxt_j);
+      tile_rows(nxt, nm0, nm1);
+      nsrc = load_rows(nm0, nm1);  // consumed in this tile's epilogue
+      // claim tile i+2 now; its value is read in the epilogue, after the K
+      // loop has waited for every load (so reading it costs no extra wait)
+      if (tid == 0) claim = (int)atomicAdd(&queue[xcd], 1u);
+    }
+    const int c0 = cur.nt * Cfg::kOutCols;
+
+    f32x16 acc[Cfg::TM][Cfg::TN];
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < Cfg::TN; ++jn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jn][r] = 0.f;
+
+    const int nb_live = max(0, min(BM / 32, (cm1 - cm0 + 31) / 32));
+    const int tm_live = min(Cfg::TM, nb_live > wm ? (nb_live - wm + WM - 1) / WM : 0);
+    bf16x8 fa[2][Cfg::TM], fb[2][Cfg::TN];
+    auto k_loop = [&](auto live_c) {
+      constexpr int LIVE = decltype(live_c)::value;
+      constexpr int NM = LIVE * Cfg::TN;
+      constexpr int NR = LIVE + Cfg::TN;
+      static_assert(NM >= NR || LIVE <= 1, "reads fit between the MFMAs");
+      auto kstep = [&](auto chk_c, int set, bool rd, const u32x4* as, const u32x4* bs,
+                       int ks_next, int kt, int lo, int hi) {
+        constexpr bool CHK = decltype(chk_c)::value;
+        const int nd = hi - lo;
+        const int lo_ = lane_off(ks_next);
+        const u32x4* asl = as + a_uni + lo_;
+        const u32x4* bsl = bs + lo_;
+        auto read_frag = [&](int jr) {
+          if (jr < LIVE)
+            fa[set ^ 1][jr] = __builtin_bit_cast(bf16x8, asl[jr * WM * 32 * CH]);
+          else
+            fb[set ^ 1][jr - LIVE] = __builtin_bit_cast(bf16x8, bsl[b_row0(jr - LIVE) * CH]);
+        };
+        auto dma_at = [&](int jm) {
+          const int np = nd / 2;
+#pragma unroll
+          for (int qd = 0; qd < LPS / 2; ++qd) {
+            if (qd >= np) break;
+            if ((NM > 0 ? qd * NM / np : 0) != jm) continue;
+            const int i = lo + 2 * qd;
+            const int nx = i < A_INS ? kt + NSA - 1 : kt + NSB - 1;
+            if (!CHK || nx < KT) dma2(i, nx, g + nx, b_base);
+          }
+        };
+        if (NM == 0) {
+          dma_at(0);
+          return;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jm = 0; jm < NM; ++jm) {
+          const int tm = jm / Cfg::TN, tn = jm % Cfg::TN;
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][tn], fa[set][tm],
+                                                                 acc[tm][tn], 0, 0, 0);
+          if (rd && jm < NR) read_frag(jm);
+          if (rd && NM < NR && jm == NM - 1)
+#pragma unroll
+            for (int r = NM; r < NR; ++r) read_frag(r);
+          dma_at(jm);
+        }
+        if (rd) {
+          constexpr int NP = NM < NR ? NM : NR;
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+          if (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto read_first = [&](const u32x4* as, const u32x4* bs) {
+        if (LIVE == 0) return;
+        const int lo_ = lane_off(0);
+#pragma unroll
+        for (int tm = 0; tm < LIVE; ++tm)
+          fa[0][tm] = __builtin_bit_cast(bf16x8, as[a_uni + lo_ + tm * WM * 32 * CH]);
+#pragma unroll
+        for (int tn = 0; tn < Cfg::TN; ++tn)
+          fb[0][tn] = __builtin_bit_cast(bf16x8, bs[lo_ + b_row0(tn) * CH]);
+      };
+      constexpr int KS = BK / 16;
+      auto slice_ready = [&](int kt) {
+        MOE_WAIT_LGKM0();
+        // As in the one-tile kernel. At a tile's slice 0 the issue order
+        // after B(0) is: B(1), the previous epilogue's pend_st stores
+        // (exactly that many: every thread issues all of them), the next
+        // tile's row-index load and the claim; so B(0) has landed once at
+        // most kFirst + pend_st remain, and the stores keep draining.
+        constexpr int kSteady = (NSB > NSA ? B_INS : 0) + (NSA - 2) * (A_INS + B_INS);
+        constexpr int kFirst = (NSB - 2) * B_INS;
+        static_assert(kSteady < 64 && kFirst + kMaxPendSt < 64, "vmcnt range");
+        if (kt == 0 && NSB - 2 < KT) {
+          if (pend_st == 2 * kStPass) MOE_WAIT_VMCNT(kFirst + 2 * kStPass);
+          else if (pend_st == kStPass) MOE_WAIT_VMCNT(kFirst + kStPass);
+          else MOE_WAIT_VMCNT(kFirst);
+        } else if (kt > 0 && kt >= NSA - 1 && kt + NSB - 2 < KT) {
+          MOE_WAIT_VMCNT(kSteady);
+        } else {
+          MOE_WAIT_VMCNT(0);
+        }
+        wg_barrier();
+      };
+      auto dlo = [](int qd) { return qd * LPS / KS; };
+      auto middle_steps = [&](auto chk_c, int kt) {
+        const u32x4* as = stA(g + kt);
+        const u32x4* bs = stB(g + kt);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks)
+          kstep(chk_c, ks & 1, true, as, bs, ks + 1, kt, dlo(ks + 1), dlo(ks + 2));
+      };
+      auto step = [&](auto chk_c, int kt) {
+        middle_steps(chk_c, kt);
+        slice_ready(kt + 1);
+        kstep(chk_c, 1, true, stA(g + kt + 1), stB(g + kt + 1), 0, kt + 1, 0, dlo(1));
+      };
+      constexpr std::false_type kNoCheck{};
+      constexpr std::true_type kCheck{};
+      slice_ready(0);
+      read_first(stA(g), stB(g));
+#pragma unroll
+      for (int i = 0; i < LPS; i += 2)
+        if (i < dlo(1)) {
+          const int nx = i < A_INS ? NSA - 1 : NSB - 1;
+          if (nx < KT) dma2(i, nx, g + nx, b_base);
+        }
+      static_assert(LPS / KS <= A_INS, "the first DMA share of a slice is A rows only");
+      constexpr int kLead = NSA > NSB - 1 ? NSA : NSB - 1;
+      int kt = 0;
+      for (; kt + kLead < KT; ++kt) step(kNoCheck, kt);
+      for (; kt + 1 < KT; ++kt) step(kCheck, kt);
+      middle_steps(kCheck, KT - 1);
+      kstep(kCheck, 1, false, stA(g), stB(g), 0, KT, 0, 0);
+    };
+    static_assert(Cfg::TM <= 4, "band-count dispatch");
+    switch (tm_live) {
+      case 0: k_loop(std::integral_constant<int, 0>{}); break;
+      case 1: k_loop(std::integral_constant<int, 1>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
+      default: k_loop(std::integral_constant<int, Cfg::TM>{}); break;
+    }
+
+    // ---- epilogue of the current tile, prologue of the next
+    MOE_WAIT_LGKM0();  // every wave's last fragment reads are done: the ring is free
+    wg_barrier();
+    // The last slice waited for every load of the wave (the row indices and
+    // the claim included) and nothing was issued since, so this costs
+    // nothing; it tells the compiler so, and the claim moves to an SGPR
+    // (otherwise the compiler waits for it where it is used, after the next
+    // tile's first loads and this tile's stores have been issued).
+    MOE_WAIT_VMCNT(0);
+    const int claim_s = __builtin_amdgcn_readfirstlane(claim);
+    const int gl = g + KT - 1;  // ring slot of the last slice: its stages stage the output
+    g += KT;
+    if (has_next) {
+      // every DMA of this tile has landed (its last slice waited for all),
+      // so the row indices loaded during the K loop are in too
+      set_aoff(nsrc);
+      set_boff(nxt.nt * Cfg::kOutCols);
+      b_base = b_base_of(nxt.e);
+      prologue(g, b_base);
+    }
+    // Output staging: rows go through the two stages of the last slice,
+    // region 0 = its A stage, region 1 = its B stage (32 KiB each), 16-byte
+    // chunks XOR-swizzled by row; then whole rows are stored, 16 bytes per
+    // lane. gate/up (h, 128 columns, 256 B a row): rows 0-127 and 128-255.
+    // down (y, 256 columns, 512 B a row): two passes of 128 rows, 64 rows
+    // per region.
+    // byte offsets of the two regions in the ring (integers, so every access
+    // below stays an LDS access the compiler can see)
+    const int rgn0 = (gl % NSA) * kStageA * 16;
+    const int rgn1 = (NSA * kStageA + (gl % NSB) * kStageB) * 16;
+    char* const ring_b = reinterpret_cast<char*>(ring);
+    constexpr int OC = Cfg::kOutCols;
+    constexpr int CPR = OC / 8;                  // 16-byte chunks per row
+    constexpr int RPR = 32768 / (OC * 2);         // rows per region
+    constexpr int PASSES = SWIGLU ? 1 : 2;
+    constexpr int PR = BM / PASSES;              // rows per pass
+    static_assert(PR == 2 * RPR, "a pass fills both regions");
+    auto ot_addr = [&](int row, int col) {  // row within the pass
+      return ring_b + (row < RPR ? rgn0 : rgn1) + (row % RPR) * (OC * 2) +
+             (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col & 7) << 1);
+    };
+    const int rows_here = cm1 - cm0;
+    const int etid = opaque_tid();
+    const int eli = etid & 31, elk = (etid >> 5) & 1;
+    constexpr int RSTEP = Cfg::kThreads / CPR;
+    constexpr int NPASS = PR / RSTEP;
+    static_assert(Cfg::kThreads % CPR == 0 && PR % RSTEP == 0 && NPASS % 8 == 0, "passes");
+    // Every thread issues all of its stores (a fixed count, which the next
+    // tile's first wait relies on): a row past the tile's last one stores
+    // the last row again and a column chunk past N0 the last chunk again,
+    // the same bytes to the same addresses. A pass with no row of the tile
+    // (down, at most 128 rows) is skipped as a whole.
+    const int oc = etid % CPR, r0 = etid / CPR;
+    const int occ = min(oc, (N0 - c0) / 8 - 1);
+    const int col = c0 + occ * 8;
+    pend_st = 0;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      if (ps && rows_here <= ps * PR) break;  // uniform
+      if (ps) wg_barrier();  // the first pass has been read out
+      constexpr int TMP = Cfg::TM / PASSES;  // bands of this wave in one pass
+#pragma unroll
+      for (int b = 0; b < TMP; ++b) {
+        const int tm = ps * TMP + b;
+        const int row = band_row(tm) - ps * PR + eli;
+        if (SWIGLU) {
+          constexpr int half = Cfg::TN / 2;
+#pragma unroll
+          for (int tg = 0; tg < half; ++tg) {
+            // the accumulators stay in AGPRs up to here (the compiler would
+            // otherwise copy all of them to VGPRs at the start of the epilogue)
+            asm volatile("" : "+a"(acc[tm][tg]), "+a"(acc[tm][tg + half]));
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              const int cc = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * elk;
+              const f32x16& u = acc[tm][tg];
+              const f32x16& v = acc[tm][tg + half];
+              uint2 pk;
+              pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]),
+                                 silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
+              pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]),
+                                 silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
+              *reinterpret_cast<uint2*>(ot_addr(row, cc)) = pk;
+            }
+            // one fragment pair at a time: the compiler would otherwise read
+            // every accumulator of the pass into VGPRs first
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < Cfg::TN; ++tn) {
+            asm volatile("" : "+a"(acc[tm][tn]));
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              const int cc = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * elk;
+              const f32x16& a = acc[tm][tn];
+              uint2 pk;
+              pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
+              pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
+              *reinterpret_cast<uint2*>(ot_addr(row, cc)) = pk;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      __syncthreads();
+      const int n0e = opaque_s(N0);
+      const int last = rows_here - 1 - ps * PR;  // last row of the tile in this pass (>= 0)
+      uint16_t* gout = C + (size_t)(cm0 + ps * PR) * n0e + col;
+#pragma unroll
+      for (int p0 = 0; p0 < NPASS; p0 += 8) {
+        u32x4 v[8];
+        int rr[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          rr[jj] = min(r0 + (p0 + jj) * RSTEP, last);
+          v[jj] = *reinterpret_cast<const u32x4*>(ot_addr(rr[jj], occ * 8));
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          *reinterpret_cast<u32x4*>(gout + (size_t)rr[jj] * n0e) = v[jj];
+      }
+      pend_st += NPASS;
+      MOE_WAIT_LGKM0();
+    }
+    if (!has_next) break;  // uniform
+    // hand the claim (tile i+2) to every wave through region 0, then move on
+    wg_barrier();  // every staged row has been read
+    if (tid == 0) *reinterpret_cast<int*>(ring_b + rgn0) = claim_s;
+    wg_barrier();
+    const int claimed = *reinterpret_cast<const int*>(ring_b + rgn0);  // read before the next
+    // tile's slice 0 barrier, after which its A(1) DMA may overwrite region 0
+    cur = nxt;
+    cm0 = nm0;
+    cm1 = nm1;
+    cur_j = nxt_j;
+    nxt_j = 2 * S + __builtin_amdgcn_readfirstlane(claimed);
+  }
+  // the last workgroup to finish leaves the queue zeroed for the next launch
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(&queue[kXcd], 1u) == gridDim.x - 1) {
+#pragma unroll
+      for (int i = 0; i <= kXcd; ++i) atomicExch(&queue[i], 0u);
+      __threadfence();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 SIMT
 
 template <bool SWIGLU>
@@ -858,8 +1410,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // from LDS per MFMA than 64 x 128 ones, which matters on a power-limited chip
 // (8 waves of 64 x 128 are ~1-3% slower here).
 constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 2, kWN = 2, kNSA = 2, kNSB = 3;
-// K slice and ring depths of the forward gate/up and down launches
+// K slice and ring depths of the forward gate/up launch that keeps u, v
 constexpr int kFBK = 64, kFNSA = 2, kFNSB = 3;
+// Workspace of the persistent forward launches: the tile queue.
+constexpr size_t kExpertWorkspaceBytes = 256;
+static_assert(kQueueWords * 4 <= kExpertWorkspaceBytes, "queue fits the workspace");
 
 // The bf16 kernel addresses its operands with 32-bit per-lane byte offsets:
 // from the activation matrix (rows x K) and from one expert's weight panel
@@ -867,6 +1422,38 @@ constexpr int kFBK = 64, kFNSA = 2, kFNSB = 3;
 inline bool dma_offsets_fit(int64_t a_rows, int64_t n0, int64_t k) {
   const int64_t lim = (int64_t(1) << 32) - kDmaBias - 16;
   return a_rows * k * 2 <= lim && n0 * k * 2 <= lim;
+}
+
+// Compute units of the current device (cached per device); the persistent
+// launches run one workgroup per CU.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices && v > 0) g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Persistent forward launch over at most `tiles_ub` tiles: S workgroups per
+// XCD, S = CUs / 8 (one per CU), fewer when there are fewer tiles.
+template <bool SWIGLU>
+moe_status launch_persistent(const uint16_t* a, const int32_t* perm_row, const int32_t* expert_off,
+                             int E, const uint16_t* b0, const uint16_t* b1, int K, int N0,
+                             uint16_t* c, uint32_t* queue, int64_t tiles_ub, hipStream_t stream) {
+  const int cus = cu_count();
+  if (cus <= 0) return MOE_ERR_DEVICE;
+  const int64_t per_xcd = ceil_div(std::max<int64_t>(tiles_ub, 1), kXcd);
+  const int S = (int)std::max<int64_t>(1, std::min<int64_t>(cus / kXcd, per_xcd));
+  hipLaunchKernelGGL(ffn_persistent_kernel<SWIGLU>, dim3(kXcd * S), dim3(256), 0, stream, a,
+                     perm_row, expert_off, E, b0, b1, K, N0, c, queue);
+  return launch_status();
 }
 
 moe_status check_ffn(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F, moe_dtype dt) {
@@ -914,6 +1501,39 @@ void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* ks
 
 using namespace moe;
 
+MOE_EXPORT size_t moe_expert_workspace_bytes(void) { return kExpertWorkspaceBytes; }
+
+MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm_row,
+                                         const int32_t* expert_off, int32_t T, int32_t E,
+                                         int32_t k, int32_t d, int32_t F, const void* w_gate,
+                                         const void* w_up, moe_dtype dt, void* h, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_ffn(T, E, k, d, F, dt);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h) return MOE_ERR_ARG;
+  if (!workspace || workspace_bytes < kExpertWorkspaceBytes || (uintptr_t)workspace % 16)
+    return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)x_disp | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)h) % 16)
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)T * k;
+  if (dt == MOE_BF16) {
+    if (!dma_offsets_fit(rows, F, d)) return MOE_ERR_UNSUPPORTED;
+    const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kBN / 2);
+    return launch_persistent<true>(static_cast<const uint16_t*>(x_disp), perm_row, expert_off, E,
+                                   static_cast<const uint16_t*>(w_gate),
+                                   static_cast<const uint16_t*>(w_up), d, F,
+                                   static_cast<uint16_t*>(h), static_cast<uint32_t*>(workspace),
+                                   tiles, stream);
+  }
+  const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 32);
+  hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(tiles)), dim3(256), 0, stream,
+                     static_cast<const float*>(x_disp), perm_row, expert_off, E,
+                     static_cast<const float*>(w_gate), static_cast<const float*>(w_up), d, F,
+                     static_cast<float*>(h), nullptr);
+  return launch_status();
+}
+
 MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t* perm_row,
                                               const int32_t* expert_off, int32_t T, int32_t E,
                                               int32_t k, int32_t d, int32_t F,
@@ -922,7 +1542,7 @@ MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t*
   moe_status st = check_ffn(T, E, k, d, F, dt);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
-  if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h) return MOE_ERR_ARG;
+  if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h || !uv) return MOE_ERR_ARG;
   if (((uintptr_t)x_disp | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)h | (uintptr_t)uv) % 16)
     return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
@@ -946,40 +1566,31 @@ MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t*
   return launch_status();
 }
 
-MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm_row,
-                                         const int32_t* expert_off, int32_t T, int32_t E,
-                                         int32_t k, int32_t d, int32_t F, const void* w_gate,
-                                         const void* w_up, moe_dtype dt, void* h,
-                                         hipStream_t stream) {
-  return moe_expert_gate_up_save(x_disp, perm_row, expert_off, T, E, k, d, F, w_gate, w_up, dt,
-                                 h, nullptr, stream);
-}
-
 MOE_EXPORT moe_status moe_expert_down(const void* h, const int32_t* expert_off, int32_t T,
                                       int32_t E, int32_t k, int32_t d, int32_t F,
-                                      const void* w_down, moe_dtype dt, void* y,
-                                      hipStream_t stream) {
+                                      const void* w_down, moe_dtype dt, void* y, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_ffn(T, E, k, d, F, dt);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!h || !expert_off || !w_down || !y) return MOE_ERR_ARG;
+  if (!workspace || workspace_bytes < kExpertWorkspaceBytes || (uintptr_t)workspace % 16)
+    return MOE_ERR_WORKSPACE;
   if (((uintptr_t)h | (uintptr_t)w_down | (uintptr_t)y) % 16) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
     if (!dma_offsets_fit(rows, d, F)) return MOE_ERR_UNSUPPORTED;
     const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(d, kBN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kFBK, kWM, kWN, kFNSA, kFNSB, false>),
-                       dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream,
-                       static_cast<const uint16_t*>(h), nullptr, expert_off, E,
-                       static_cast<const uint16_t*>(w_down), nullptr, F, d,
-                       static_cast<uint16_t*>(y), nullptr);
-  } else {
-    const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(d, 64);
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid_for(tiles)), dim3(256), 0, stream,
-                       static_cast<const float*>(h), nullptr, expert_off, E,
-                       static_cast<const float*>(w_down), nullptr, F, d, static_cast<float*>(y),
-                       nullptr);
+    return launch_persistent<false>(static_cast<const uint16_t*>(h), nullptr, expert_off, E,
+                                    static_cast<const uint16_t*>(w_down), nullptr, F, d,
+                                    static_cast<uint16_t*>(y), static_cast<uint32_t*>(workspace),
+                                    tiles, stream);
   }
+  const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(d, 64);
+  hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid_for(tiles)), dim3(256), 0, stream,
+                     static_cast<const float*>(h), nullptr, expert_off, E,
+                     static_cast<const float*>(w_down), nullptr, F, d, static_cast<float*>(y),
+                     nullptr);
   return launch_status();
 }
 
@@ -987,9 +1598,11 @@ MOE_EXPORT moe_status moe_grouped_ffn(const void* x_disp, const int32_t* perm_ro
                                       const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
                                       int32_t d, int32_t F, const void* w_gate, const void* w_up,
                                       const void* w_down, moe_dtype dt, void* h, void* y,
+                                      void* workspace, size_t workspace_bytes,
                                       hipStream_t stream) {
   moe_status st = moe_expert_gate_up(x_disp, perm_row, expert_off, T, E, k, d, F, w_gate, w_up,
-                                     dt, h, stream);
+                                     dt, h, workspace, workspace_bytes, stream);
   if (st != MOE_OK) return st;
-  return moe_expert_down(h, expert_off, T, E, k, d, F, w_down, dt, y, stream);
+  return moe_expert_down(h, expert_off, T, E, k, d, F, w_down, dt, y, workspace, workspace_bytes,
+                         stream);
 }

@@ -47,11 +47,13 @@ def lib():
             "moe_dispatch_workspace_bytes": (sz, [i32, i32, i32, i32]),
             "moe_dispatch_layout": (C.c_int, [p, i32, i32, i32, p, i32, p, i32, C.c_int,
                                               p, p, p, p, p, p, p, p, sz, p]),
+            "moe_expert_workspace_bytes": (sz, []),
             "moe_expert_gate_up": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p, C.c_int,
-                                             p, p]),
-            "moe_expert_down": (C.c_int, [p, p, i32, i32, i32, i32, i32, p, C.c_int, p, p]),
+                                             p, p, sz, p]),
+            "moe_expert_down": (C.c_int, [p, p, i32, i32, i32, i32, i32, p, C.c_int, p, p, sz,
+                                          p]),
             "moe_grouped_ffn": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p, p, C.c_int,
-                                          p, p, p]),
+                                          p, p, p, sz, p]),
             "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
             "moe_plan_placement": (C.c_int, [p, p, i32, i32, i32, i32, p]),
             "moe_expert_gate_up_save": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p,
@@ -246,33 +248,45 @@ def moe_token_shuffle(want_idx, aff, x=None, out=None, stream=None):
     return out
 
 
-def moe_expert_gate_up(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=None, stream=None):
+def expert_workspace(device):
+    """A zero-filled workspace for the forward expert calls (they leave it
+    zero-filled, so one buffer serves every call on one stream)."""
+    return torch.zeros(max(16, int(lib().moe_expert_workspace_bytes())), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_expert_gate_up(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=None, workspace=None,
+                       stream=None):
     E, F, d = w_gate.shape
     h = torch.empty((T * k, F), dtype=x_disp.dtype, device=x_disp.device) if h is None else h
+    ws = expert_workspace(x_disp.device) if workspace is None else workspace
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
-        dtype_code(x_disp), _ptr(h), _stream(stream)))
+        dtype_code(x_disp), _ptr(h), _ptr(ws), ws.numel(), _stream(stream)))
     return h
 
 
-def moe_expert_down(h, expert_off, T, k, w_down, y=None, stream=None):
+def moe_expert_down(h, expert_off, T, k, w_down, y=None, workspace=None, stream=None):
     E, d, F = w_down.shape
     y = torch.empty((T * k, d), dtype=h.dtype, device=h.device) if y is None else y
+    ws = expert_workspace(h.device) if workspace is None else workspace
     _check("moe_expert_down", lib().moe_expert_down(
-        _ptr(h), _ptr(expert_off), T, E, k, d, F, _ptr(w_down), dtype_code(h), _ptr(y),
-        _stream(stream)))
+        _ptr(h), _ptr(expert_off), T, E, k, d, F, _ptr(w_down), dtype_code(h), _ptr(y), _ptr(ws),
+        ws.numel(), _stream(stream)))
     return y
 
 
 def moe_grouped_ffn(x_disp, perm_row, expert_off, T, k, w_gate, w_up, w_down, h=None, y=None,
-                    stream=None):
+                    workspace=None, stream=None):
     E, F, d = w_gate.shape
     dev, dt = x_disp.device, x_disp.dtype
     h = torch.empty((T * k, F), dtype=dt, device=dev) if h is None else h
     y = torch.empty((T * k, d), dtype=dt, device=dev) if y is None else y
+    ws = expert_workspace(dev) if workspace is None else workspace
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), dtype_code(x_disp), _ptr(h), _ptr(y), _stream(stream)))
+        _ptr(w_down), dtype_code(x_disp), _ptr(h), _ptr(y), _ptr(ws), ws.numel(),
+        _stream(stream)))
     return h, y
 
 
@@ -427,6 +441,7 @@ class Layer:
         self.coact = torch.zeros((E, E), dtype=torch.int32, device=dev)
         self.lay = alloc_layout(T, E, k, G, dev, d, dtype)
         self.h = torch.empty((T * k, F), dtype=dtype, device=dev)
+        self.expert_ws = expert_workspace(dev)
         self.y = torch.empty((T * k, d), dtype=dtype, device=dev)
         self.out = torch.empty((T, d), dtype=dtype, device=dev)
 
@@ -442,10 +457,11 @@ class Layer:
 
     def gate_up(self, w_gate, w_up, stream=None):
         moe_expert_gate_up(self.lay["x_disp"], self.lay["perm_row"], self.lay["expert_off"],
-                           self.T, self.k, w_gate, w_up, self.h, stream)
+                           self.T, self.k, w_gate, w_up, self.h, self.expert_ws, stream)
 
     def down(self, w_down, stream=None):
-        moe_expert_down(self.h, self.lay["expert_off"], self.T, self.k, w_down, self.y, stream)
+        moe_expert_down(self.h, self.lay["expert_off"], self.T, self.k, w_down, self.y,
+                        self.expert_ws, stream)
 
     def combine(self, stream=None):
         moe_combine(self.y, self.lay["slot_of"], self.gates, self.T, self.k, self.out, stream)

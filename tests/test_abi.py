@@ -15,13 +15,13 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = ops.header_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert ops.status_str(0) == "ok"
     assert "workspace" in ops.status_str(3)
     assert ops.status_str(99) == "unknown status"
@@ -92,19 +92,26 @@ def test_layout_argument_errors(L):
 
 def test_ffn_and_combine_argument_errors(L):
     p = 16
-    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 100, 64, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 96, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_gate_up(None, p, p, 4, 8, 2, 64, 64, p, p, 1, p, None) == ops.MOE_ERR_ARG
-    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 64, p, p, 5, p, None) == ops.MOE_ERR_ARG
-    assert L.moe_expert_down(p, p, 4, 8, 9, 64, 64, p, 1, p, None) == ops.MOE_ERR_ARG
-    assert L.moe_expert_down(None, p, 4, 8, 2, 64, 64, p, 1, p, None) == ops.MOE_ERR_ARG
-    assert L.moe_grouped_ffn(p, p, p, 0, 8, 2, 64, 64, p, p, p, 1, p, p, None) == ops.MOE_OK
+    W = L.moe_expert_workspace_bytes()
+    assert W >= 64
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 100, 64, p, p, 1, p, p, W, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 96, p, p, 1, p, p, W, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(None, p, p, 4, 8, 2, 64, 64, p, p, 1, p, p, W, None) == ops.MOE_ERR_ARG
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 64, p, p, 5, p, p, W, None) == ops.MOE_ERR_ARG
+    assert L.moe_expert_down(p, p, 4, 8, 9, 64, 64, p, 1, p, p, W, None) == ops.MOE_ERR_ARG
+    assert L.moe_expert_down(None, p, 4, 8, 2, 64, 64, p, 1, p, p, W, None) == ops.MOE_ERR_ARG
+    assert L.moe_grouped_ffn(p, p, p, 0, 8, 2, 64, 64, p, p, p, 1, p, p, p, W, None) == ops.MOE_OK
+    # the workspace (the persistent launches' tile queue) is checked before any launch
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 64, p, p, 1, p, None, W, None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 64, 64, p, p, 1, p, p, W - 1, None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_expert_down(p, p, 4, 8, 2, 64, 64, p, 1, p, None, W, None) == ops.MOE_ERR_WORKSPACE
+    assert L.moe_expert_down(p, p, 4, 8, 2, 64, 64, p, 1, p, 8, W, None) == ops.MOE_ERR_WORKSPACE  # unaligned
     # bf16 operands addressed with 32-bit offsets: 2^20 * 8 slots x 4096 bf16
     # activations (64 GiB) and a 2^20 x 4096 weight panel are refused up front
     big_t = 1 << 20
-    assert L.moe_expert_gate_up(p, p, p, big_t, 8, 8, 4096, 64, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_down(p, p, big_t, 8, 8, 64, 4096, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 4096, 1 << 20, p, p, 1, p, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(p, p, p, big_t, 8, 8, 4096, 64, p, p, 1, p, p, W, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down(p, p, big_t, 8, 8, 64, 4096, p, 1, p, p, W, None) == ops.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up(p, p, p, 4, 8, 2, 4096, 1 << 20, p, p, 1, p, p, W, None) == ops.MOE_ERR_UNSUPPORTED
     assert L.moe_combine(p, p, p, 4, 0, 64, 1, p, None) == ops.MOE_ERR_ARG
     assert L.moe_combine(p, p, p, 4, 2, 4, 1, p, None) == ops.MOE_ERR_UNSUPPORTED  # 8-byte rows
     assert L.moe_combine(None, p, p, 4, 2, 64, 1, p, None) == ops.MOE_ERR_ARG

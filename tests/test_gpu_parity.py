@@ -234,6 +234,43 @@ def test_ffn_alone_on_oracle_layout():
 
 
 
+def test_expert_workspace_is_left_zero_and_reused():
+    """The persistent expert launches claim tiles from a queue in the caller's
+    workspace and leave it zero-filled: two calls in a row on one workspace
+    give bit-identical h and y (a stale counter would skip tiles, leaving the
+    NaN the outputs start as), and the workspace reads back as zeros. The
+    shape has more tiles than two rounds of workgroups, so tiles are
+    claimed from the queue."""
+    rng = np.random.default_rng(41)
+    T, k, E, d, F = 4096, 4, 8, 2048, 1536
+    S = T * k
+    counts = rng.multinomial(S, rng.dirichlet(np.ones(E)))
+    eo = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = 9000
+    perm = rng.integers(0, R, S).astype(np.int32)
+    bf = synth.f32_to_bf16_bits
+    x_disp = dev(bf(rng.standard_normal((R, d), dtype=np.float32)))
+    wg = dev(bf(rng.standard_normal((E, F, d), dtype=np.float32) / np.sqrt(d)))
+    wu = dev(bf(rng.standard_normal((E, F, d), dtype=np.float32) / np.sqrt(d)))
+    wd = dev(bf(rng.standard_normal((E, d, F), dtype=np.float32) / np.sqrt(F)))
+    ws = ops.expert_workspace("cuda")
+    outs = []
+    for _ in range(2):
+        h = torch.full((S, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+        y = torch.full((S, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ops.moe_grouped_ffn(x_disp, dev(perm), dev(eo), T, k, wg, wu, wd, h, y, workspace=ws)
+        torch.cuda.synchronize()
+        assert not host(ws).any(), "workspace not left zero-filled"
+        outs.append((host(h), host(y)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    slots = band_sample(eo)
+    sexp = oracle.slot_experts(eo)[slots]
+    y_ref, h_ref = oracle.ffn_rows(host(x_disp), perm[slots], sexp, host(wg), host(wu), host(wd),
+                                   want_h=True)
+    assert_close("h(bands)", outs[0][0][slots], h_ref, TAU["bf16"])
+    assert_close("y(bands)", outs[0][1][slots], y_ref, TAU["bf16"])
+
+
 # Segment lengths at every boundary of how a grouped launch cuts an expert's
 # rows into 256-row m-tiles of whole 32-row bands split evenly over the
 # expert: empty, one row, around one band, around one m-tile, two and three
