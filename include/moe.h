@@ -121,7 +121,11 @@ size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t G);
  *  slot_of   [T*k] int32: slot of (token t, choice j) at index t*k+j.
  *  x_disp    [T*k,d] (dt): rows 0..R-1 get x[disp_token[r]]; ignored if
  *            x is NULL.
- *  workspace: device scratch of at least moe_dispatch_workspace_bytes().
+ *  workspace: device scratch of at least moe_dispatch_workspace_bytes(),
+ *            16-byte aligned, ZERO-FILLED before its first use: its first
+ *            256 bytes hold a counter that the call's last count block uses
+ *            and sets back to zero, so every call leaves it zero-filled.
+ *            Calls that may run at the same time need separate workspaces.
  * R stays on the device; nothing is copied back to the host.
  */
 moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
@@ -141,9 +145,12 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t E, in
  * until the process ends); the call allocates nothing. Returns
  * MOE_ERR_WORKSPACE, enqueuing nothing, when the scratch the shape needs
  * (moe_dispatch_workspace_bytes(T, E, k, G)) exceeds that size; e.g.
- * T = 16384, E = 256, G = 32 needs 1.3 MB. Every call on a GPU shares that
- * GPU's scratch: calls that may overlap in time on one GPU (other streams,
- * other host threads) race and must be serialised by the caller.
+ * T = 16384, E = 256, G = 32 needs 1.3 MB. The scratch starts zero-filled
+ * (device memory of static storage) and every call leaves its counter word
+ * at zero again, as moe_dispatch_layout requires of its workspace. Every
+ * call on a GPU shares that GPU's scratch: calls that may overlap in time
+ * on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.
  */
 #define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
 moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
@@ -214,7 +221,9 @@ size_t moe_shuffle_workspace_bytes(int32_t T, int32_t G);
  *           ascending within a rank).
  *  pos      [T] int32: position of token t in that order (perm[pos[t]] = t).
  *  x_shuf   [T,d] (dt): x[perm[i]] in row i; ignored if x is NULL.
- *  workspace: device scratch of at least moe_shuffle_workspace_bytes().
+ *  workspace: device scratch of at least moe_shuffle_workspace_bytes(),
+ *           16-byte aligned and zero-filled before its first use, as for
+ *           moe_dispatch_layout (every call leaves it so).
  * G <= 32, k <= 16.
  */
 moe_status moe_token_shuffle(const int32_t* want_idx, int32_t T, int32_t E, int32_t k,

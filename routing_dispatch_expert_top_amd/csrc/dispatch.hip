@@ -15,10 +15,10 @@
 // bitmaps (key = expert or rank, 8 words of 32 tokens each) with atomicOr,
 // which commutes, so the bitmaps do not depend on timing. The stable rank of
 // a token among the block's tokens with the same key is the popcount of the
-// bits before it. Three launches:
+// bits before it. Two launches:
 //   count : per-block key counts, the bitmaps and their per-word prefix
-//           counts (to the workspace), and rank_mask;
-//   scan  : one workgroup turns the counts into per-block bases and the
+//           counts (to the workspace), and rank_mask; the last block to
+//           finish turns the counts into per-block bases and the
 //           expert_off / rank_off prefixes (no host round trip: R stays on
 //           the device);
 //   token : one wavefront per token finds its rows and slots from the
@@ -71,34 +71,6 @@ __device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk
   return m;
 }
 
-// Per block and key q (experts 0..E-1, then ranks): cnt[b][q] = tokens of
-// block b with key q; wmask[b][q][w] = the key's bitmap word w and
-// wpre[b][q][w] = popcount of words 0..w-1 (a token's rank within the block
-// is wpre + popcount of the bits before it in its word).
-__global__ __launch_bounds__(kBlockTok) void layout_count_kernel(
-    const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
-    const int32_t* __restrict__ rank_of, int G, uint32_t* __restrict__ rank_mask,
-    int32_t* __restrict__ cnt, uint32_t* __restrict__ wmask, int32_t* __restrict__ wpre) {
-  __shared__ BlockMasks sm;
-  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, rank_of, G);
-  const int t = blockIdx.x * kBlockTok + threadIdx.x;
-  if (t < T) rank_mask[t] = m;
-  const int Q = E + G;
-  uint32_t* wm = wmask + (size_t)blockIdx.x * Q * kWords;
-  int32_t* wp = wpre + (size_t)blockIdx.x * Q * kWords;
-  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
-    const uint32_t* mk = q < E ? &sm.emask[q * kWords] : &sm.rmask[(q - E) * kWords];
-    int c = 0;
-#pragma unroll
-    for (int w = 0; w < kWords; ++w) {
-      wm[q * kWords + w] = mk[w];
-      wp[q * kWords + w] = c;
-      c += __popc(mk[w]);
-    }
-    cnt[(size_t)blockIdx.x * Q + q] = c;
-  }
-}
-
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
@@ -130,18 +102,25 @@ __device__ void wave_excl_scan_256(const int32_t* in, int32_t* out, int n, int32
   if (lane == kWave - 1) *total = incl;
 }
 
-// One workgroup: per-key totals over the blocks, the two exclusive scans,
-// then per-block bases. A thread owns one key and walks the blocks in chunks
-// of kScanChunk whose loads are all issued before any is used, so the walk
-// costs nblk / kScanChunk memory round trips instead of nblk.
+// Per-key totals over the blocks, the two exclusive scans, then per-block
+// bases, by one workgroup (the last count block to finish). A thread owns a
+// key and walks the blocks in chunks of kScanChunk whose loads are all
+// issued before any is used, so the walk costs nblk / kScanChunk memory
+// round trips instead of nblk. The counts are read with device-coherent
+// loads: other workgroups wrote them.
 constexpr int kScanChunk = 8;
 
-__global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__ cnt, int nblk,
-                                                           int E, int G,
-                                                           int32_t* __restrict__ expert_off,
-                                                           int32_t* __restrict__ rank_off) {
-  __shared__ int32_t tot[kMaxE + kMaxG];
-  __shared__ int32_t off[kMaxE + kMaxG];
+__device__ __forceinline__ int load_cnt(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct ScanSmem {
+  int32_t tot[kMaxE + kMaxG];
+  int32_t off[kMaxE + kMaxG];
+};
+
+__device__ void scan_blocks(ScanSmem& sm, int32_t* __restrict__ cnt, int nblk, int E, int G,
+                            int32_t* __restrict__ expert_off, int32_t* __restrict__ rank_off) {
   const int Q = E + G;
   for (int q = threadIdx.x; q < Q; q += blockDim.x) {
     int s = 0;
@@ -149,26 +128,26 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
       int c[kScanChunk];
 #pragma unroll
       for (int i = 0; i < kScanChunk; ++i)
-        c[i] = b0 + i < nblk ? cnt[(size_t)(b0 + i) * Q + q] : 0;
+        c[i] = b0 + i < nblk ? load_cnt(&cnt[(size_t)(b0 + i) * Q + q]) : 0;
 #pragma unroll
       for (int i = 0; i < kScanChunk; ++i) s += c[i];
     }
-    tot[q] = s;
+    sm.tot[q] = s;
   }
   __syncthreads();
   const int wave = threadIdx.x / kWave;
-  if (wave == 0) wave_excl_scan_256(tot, off, E, &expert_off[E]);
-  if (wave == 1) wave_excl_scan_256(tot + E, off + E, G, &rank_off[G]);
+  if (wave == 0) wave_excl_scan_256(sm.tot, sm.off, E, &expert_off[E]);
+  if (wave == 1) wave_excl_scan_256(sm.tot + E, sm.off + E, G, &rank_off[G]);
   __syncthreads();
   for (int q = threadIdx.x; q < Q; q += blockDim.x) {
-    int run = off[q];
+    int run = sm.off[q];
     if (q < E) expert_off[q] = run;
     else rank_off[q - E] = run;
     for (int b0 = 0; b0 < nblk; b0 += kScanChunk) {
       int c[kScanChunk];
 #pragma unroll
       for (int i = 0; i < kScanChunk; ++i)
-        c[i] = b0 + i < nblk ? cnt[(size_t)(b0 + i) * Q + q] : 0;
+        c[i] = b0 + i < nblk ? load_cnt(&cnt[(size_t)(b0 + i) * Q + q]) : 0;
 #pragma unroll
       for (int i = 0; i < kScanChunk; ++i) {
         if (b0 + i < nblk) cnt[(size_t)(b0 + i) * Q + q] = run;
@@ -176,6 +155,65 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(int32_t* __restrict__
       }
     }
   }
+}
+
+// An empty batch: no count blocks, so one workgroup writes the zero offsets.
+__global__ __launch_bounds__(256) void layout_empty_kernel(int E, int G,
+                                                           int32_t* __restrict__ expert_off,
+                                                           int32_t* __restrict__ rank_off) {
+  for (int q = threadIdx.x; q <= E; q += blockDim.x) expert_off[q] = 0;
+  for (int q = threadIdx.x; q <= G; q += blockDim.x) rank_off[q] = 0;
+}
+
+// Per block and key q (experts 0..E-1, then ranks): cnt[b][q] = tokens of
+// block b with key q; wmask[b][q][w] = the key's bitmap word w and
+// wpre[b][q][w] = popcount of words 0..w-1 (a token's rank within the block
+// is wpre + popcount of the bits before it in its word).
+// The last block to finish (a counter in the workspace, which that block
+// sets back to zero) then turns the counts into per-block bases and the
+// expert / rank offsets, so the layout needs no separate scan launch.
+__global__ __launch_bounds__(kBlockTok) void layout_count_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int E, int k, const int32_t* __restrict__ place,
+    const int32_t* __restrict__ rank_of, int G, uint32_t* __restrict__ rank_mask,
+    int32_t* __restrict__ cnt, uint32_t* __restrict__ wmask, int32_t* __restrict__ wpre,
+    uint32_t* __restrict__ done, int32_t* __restrict__ expert_off,
+    int32_t* __restrict__ rank_off) {
+  __shared__ BlockMasks sm;
+  __shared__ ScanSmem ssm;
+  __shared__ int last;
+  const uint32_t m = build_masks(sm, topk_idx, T, E, k, place, rank_of, G);
+  const int t = blockIdx.x * kBlockTok + threadIdx.x;
+  if (t < T) rank_mask[t] = m;
+  const int Q = E + G;
+  uint32_t* wm = wmask + (size_t)blockIdx.x * Q * kWords;
+  int32_t* wp = wpre + (size_t)blockIdx.x * Q * kWords;
+  for (int q = threadIdx.x; q < Q; q += blockDim.x) {
+    const uint32_t* mk = q < E ? &sm.emask[q * kWords] : &sm.rmask[(q - E) * kWords];
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) {
+      wm[q * kWords + w] = mk[w];
+      wp[q * kWords + w] = c;
+      c += __popc(mk[w]);
+    }
+    // device-scope store: written through to where other XCDs' device-scope
+    // loads read it (a release fence would instead write back this XCD's
+    // whole L2, which costs more than the scan saves)
+    __hip_atomic_store(&cnt[(size_t)blockIdx.x * Q + q], c, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every count of this block has been written through (the stores are
+  // complete) before the block is counted as finished
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;  // uniform
+  scan_blocks(ssm, cnt, gridDim.x, E, G, expert_off, rank_off);
+  if (threadIdx.x == 0)  // zero again for the next call
+    __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wavefront per token. Lane i < n handles the token's i-th rank (in
@@ -391,17 +429,20 @@ __global__ __launch_bounds__(256) void token_dest_kernel(
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Workspace: the finished-block counter (first 256 bytes; zero before the
+// first call, and every call leaves it zero), then per-block key counts
+// (turned into bases), the key bitmaps and their word prefixes.
 struct Workspace {
-  size_t cnt_bytes, mask_bytes, total;
+  size_t done_bytes, cnt_bytes, mask_bytes, total;
 };
 inline Workspace workspace_layout(int32_t T, int32_t E, int32_t k, int32_t G) {
   (void)k;
   Workspace w;
   const size_t nblk = (size_t)ceil_div(T, kBlockTok);
+  w.done_bytes = kAlign;
   w.cnt_bytes = align_up(nblk * (size_t)(E + G) * sizeof(int32_t));
   w.mask_bytes = align_up(nblk * (size_t)(E + G) * kWords * sizeof(uint32_t));
-  w.total = w.cnt_bytes + 2 * w.mask_bytes;  // counts, bitmaps, word prefixes
-  if (w.total == 0) w.total = kAlign;
+  w.total = w.done_bytes + w.cnt_bytes + 2 * w.mask_bytes;
   return w;
 }
 
@@ -434,17 +475,21 @@ moe_status layout_impl(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
   }
   const Workspace ws = workspace_layout(T, E, k, G);
   if (!workspace || workspace_bytes < ws.total) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)workspace % 16) return MOE_ERR_WORKSPACE;
   char* wsp = static_cast<char*>(workspace);
-  int32_t* cnt = reinterpret_cast<int32_t*>(wsp);
-  uint32_t* wmask = reinterpret_cast<uint32_t*>(wsp + ws.cnt_bytes);
-  int32_t* wpre = reinterpret_cast<int32_t*>(wsp + ws.cnt_bytes + ws.mask_bytes);
+  uint32_t* done = reinterpret_cast<uint32_t*>(wsp);
+  int32_t* cnt = reinterpret_cast<int32_t*>(wsp + ws.done_bytes);
+  uint32_t* wmask = reinterpret_cast<uint32_t*>(wsp + ws.done_bytes + ws.cnt_bytes);
+  int32_t* wpre = reinterpret_cast<int32_t*>(wsp + ws.done_bytes + ws.cnt_bytes + ws.mask_bytes);
   const int nblk = (int)ceil_div(T, kBlockTok);
 
   if (nblk > 0)
     hipLaunchKernelGGL(layout_count_kernel, dim3(nblk), dim3(kBlockTok), 0, stream, topk_idx, T,
-                       E, k, place, rank_of, G, rank_mask, cnt, wmask, wpre);
-  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, nblk, E, G,
-                     expert_off, rank_off);
+                       E, k, place, rank_of, G, rank_mask, cnt, wmask, wpre, done, expert_off,
+                       rank_off);
+  else
+    hipLaunchKernelGGL(layout_empty_kernel, dim3(1), dim3(256), 0, stream, E, G, expert_off,
+                       rank_off);
   if (nblk > 0) {
     const int row_vecs = x ? (int)((size_t)d * dtype_bytes(dt) / 16) : 0;
     hipLaunchKernelGGL(dispatch_token_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
@@ -477,13 +522,15 @@ MOE_EXPORT moe_status moe_dispatch_layout(const int32_t* topk_idx, int32_t T, in
 namespace moe {
 namespace {
 
-// Scratch of moe_dispatch_layout_noalloc: the layout workspace (per-block key
-// counts, bitmaps and their word prefixes) in a file-scope device array, so
-// that call allocates nothing. Each device holds its own copy at its own
-// address until the process ends; host code uses the address
-// hipGetSymbolAddress returns on that device, never the array's name (a
-// host-side stand-in). Every call writes all of the scratch it later reads,
-// so nothing in it has to start at zero.
+// Scratch of moe_dispatch_layout_noalloc: the layout workspace (the
+// finished-block counter, per-block key counts, bitmaps and their word
+// prefixes) in a file-scope device array, so that call allocates nothing.
+// Each device holds its own copy at its own address until the process ends;
+// host code uses the address hipGetSymbolAddress returns on that device,
+// never the array's name (a host-side stand-in). The counter must start at
+// zero: the array does (static storage is zero-filled when the code object
+// loads), and every call sets it back to zero; everything else is written
+// before it is read.
 constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
 static_assert(kNoAllocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "header and library agree");
 __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];

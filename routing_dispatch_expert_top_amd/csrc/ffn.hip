@@ -1291,13 +1291,16 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     cur_j = nxt_j;
     nxt_j = 2 * S + __builtin_amdgcn_readfirstlane(claimed);
   }
-  // the last workgroup to finish leaves the queue zeroed for the next launch
+  // The last workgroup to finish leaves the queue zeroed for the next
+  // launch. Every workgroup's claims have returned (their values were used)
+  // before it counts itself finished, so no claim can follow the reset; no
+  // fence is needed (one would write back the XCD's whole L2).
   if (tid == 0) {
-    __threadfence();
-    if (atomicAdd(&queue[kXcd], 1u) == gridDim.x - 1) {
+    if (__hip_atomic_fetch_add(&queue[kXcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        gridDim.x - 1) {
 #pragma unroll
-      for (int i = 0; i <= kXcd; ++i) atomicExch(&queue[i], 0u);
-      __threadfence();
+      for (int i = 0; i <= kXcd; ++i)
+        __hip_atomic_store(&queue[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

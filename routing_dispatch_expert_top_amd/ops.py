@@ -153,13 +153,15 @@ def moe_dispatch_workspace_bytes(T, E, k, G):
 
 
 def alloc_layout(T, E, k, G, device, d=None, dtype=None):
-    """Output buffers of moe_dispatch_layout, sized for the T*k upper bound."""
+    """Output buffers of moe_dispatch_layout, sized for the T*k upper bound,
+    and its workspace (zero-filled before its first use, as the call needs;
+    every call leaves it so)."""
     i32 = dict(dtype=torch.int32, device=device)
     out = dict(rank_mask=torch.empty(T, dtype=torch.int32, device=device),
                rank_off=torch.empty(G + 1, **i32), disp_token=torch.empty(T * k, **i32),
                expert_off=torch.empty(E + 1, **i32), perm_row=torch.empty(T * k, **i32),
                slot_of=torch.empty(T * k, **i32),
-               workspace=torch.empty(max(1, moe_dispatch_workspace_bytes(T, E, k, G)),
+               workspace=torch.zeros(max(1, moe_dispatch_workspace_bytes(T, E, k, G)),
                                      dtype=torch.uint8, device=device))
     if d is not None:
         out["x_disp"] = torch.empty((T * k, d), dtype=dtype, device=device)
@@ -234,7 +236,7 @@ def moe_token_shuffle(want_idx, aff, x=None, out=None, stream=None):
         i32 = dict(dtype=torch.int32, device=dev)
         out = dict(dest=torch.empty(T, **i32), rank_off=torch.empty(G + 1, **i32),
                    perm=torch.empty(T, **i32), pos=torch.empty(T, **i32),
-                   workspace=torch.empty(max(1, int(lib().moe_shuffle_workspace_bytes(T, G))),
+                   workspace=torch.zeros(max(1, int(lib().moe_shuffle_workspace_bytes(T, G))),
                                          dtype=torch.uint8, device=dev))
         if x is not None:
             out["x_shuf"] = torch.empty_like(x)

@@ -234,6 +234,28 @@ def test_ffn_alone_on_oracle_layout():
 
 
 
+def test_layout_workspace_is_left_zero():
+    """The layout's last count block scans the counts and sets its counter in
+    the workspace back to zero: the counter word reads back as zero after
+    each call, and a second call on the same workspace gives the same
+    layout (a stale counter would leave the bases unscanned)."""
+    w = synth.with_shape(synth.workload(3), T=3000)
+    inp = synth.make(w, place="contiguous", with_weights=False)
+    idx, _ = oracle.route(inp["logits"], w.k)
+    ref = oracle.layout(idx, w.E, inp["place"], w.G)
+    out = ops.alloc_layout(w.T, w.E, w.k, w.G, "cuda")
+    for _ in range(2):
+        ops.moe_dispatch_layout(dev(idx), w.E, dev(inp["place"]), w.G, out=out)
+        torch.cuda.synchronize()
+        assert not host(out["workspace"][:256]).any()
+        R = int(out["rank_off"][w.G].item())
+        g = dict(rank_mask=host(out["rank_mask"]).view(np.uint32), rank_off=host(out["rank_off"]),
+                 disp_token=host(out["disp_token"][:R]), expert_off=host(out["expert_off"]),
+                 perm_row=host(out["perm_row"]), slot_of=host(out["slot_of"]))
+        compare_exact(g, ref, ("rank_mask", "rank_off", "disp_token", "expert_off", "perm_row",
+                               "slot_of"))
+
+
 def test_expert_workspace_is_left_zero_and_reused():
     """The persistent expert launches claim tiles from a queue in the caller's
     workspace and leave it zero-filled: two calls in a row on one workspace
