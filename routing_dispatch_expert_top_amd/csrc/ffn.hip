@@ -879,6 +879,15 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     asm volatile("" : "+v"(t));
     return t;
   };
+  // An accumulator element read into a VGPR where it is used: as an asm
+  // statement the read keeps its place, so the compiler neither copies every
+  // accumulator to VGPRs at the start of the epilogue nor moves them between
+  // AGPRs (which a pin of each fragment before its use costs).
+  auto acc_read = [](float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+  };
   // the same for uniform values (e.g. the row strides of the output stores)
   auto opaque_s = [&](int v) {
     asm volatile("" : "+s"(v));
@@ -1222,19 +1231,18 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
           constexpr int half = Cfg::TN / 2;
 #pragma unroll
           for (int tg = 0; tg < half; ++tg) {
-            // the accumulators stay in AGPRs up to here (the compiler would
-            // otherwise copy all of them to VGPRs at the start of the epilogue)
-            asm volatile("" : "+a"(acc[tm][tg]), "+a"(acc[tm][tg + half]));
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
               const int cc = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * elk;
-              const f32x16& u = acc[tm][tg];
-              const f32x16& v = acc[tm][tg + half];
+              float u[4], v[4];
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) {
+                u[e4] = acc_read(acc[tm][tg][4 * qd + e4]);
+                v[e4] = acc_read(acc[tm][tg + half][4 * qd + e4]);
+              }
               uint2 pk;
-              pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]),
-                                 silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
-              pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]),
-                                 silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
+              pk.x = pack_bf16x2(silu_mul(u[0], v[0]), silu_mul(u[1], v[1]));
+              pk.y = pack_bf16x2(silu_mul(u[2], v[2]), silu_mul(u[3], v[3]));
               *reinterpret_cast<uint2*>(ot_addr(row, cc)) = pk;
             }
             // one fragment pair at a time: the compiler would otherwise read
@@ -1244,14 +1252,15 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         } else {
 #pragma unroll
           for (int tn = 0; tn < Cfg::TN; ++tn) {
-            asm volatile("" : "+a"(acc[tm][tn]));
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
               const int cc = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * elk;
-              const f32x16& a = acc[tm][tn];
+              float a[4];
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) a[e4] = acc_read(acc[tm][tn][4 * qd + e4]);
               uint2 pk;
-              pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
-              pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
+              pk.x = pack_bf16x2(a[0], a[1]);
+              pk.y = pack_bf16x2(a[2], a[3]);
               *reinterpret_cast<uint2*>(ot_addr(row, cc)) = pk;
             }
             __builtin_amdgcn_sched_barrier(0);

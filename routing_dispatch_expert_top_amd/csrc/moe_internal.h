@@ -34,8 +34,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // two bf16 packed in a 32-bit word: low half first
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Two floats to two bf16 (RNE) in one word, low half first: one
+// v_cvt_pk_bf16_f32 (converting each on its own costs two conversions, a
+// shift and an or).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t r = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 inline moe_status launch_status() {
