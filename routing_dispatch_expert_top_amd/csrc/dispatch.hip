@@ -283,26 +283,22 @@ __global__ __launch_bounds__(256) void dispatch_token_kernel(
   if (g >= 0) perm_row[s] = grow;
   if (lane < k) slot_of[(size_t)t * k + lane] = g >= 0 ? s : -1;  // -1: dropped choice
   if (!x) return;
-  u32x4* dst[kMaxK];  // n <= k <= kMaxK
-#pragma unroll
-  for (int i = 0; i < kMaxK; ++i)
-    if (i < n) dst[i] = x_disp + (size_t)__builtin_amdgcn_readlane(row, i) * row_vecs;
+  // One register set for the row: later chunks (rows longer than 8 KiB)
+  // reload into it, so the kernel keeps more wavefronts in flight.
   for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
-    u32x4 v[U];
+    if (c0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c0 == 0) v[u] = v0[u];
-      else if (c < row_vecs) v[u] = __builtin_nontemporal_load(src + c);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < row_vecs) v0[u] = __builtin_nontemporal_load(src + c);
+      }
     }
+    for (int i = 0; i < n; ++i) {
+      u32x4* dst = x_disp + (size_t)__builtin_amdgcn_readlane(row, i) * row_vecs;
 #pragma unroll
-    for (int i = 0; i < kMaxK; ++i) {
-      if (i < n) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * kWave + lane;
-          if (c < row_vecs) dst[i][c] = v[u];
-        }
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < row_vecs) dst[c] = v0[u];
       }
     }
   }

@@ -1180,8 +1180,32 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       set_aoff(nsrc);
       set_boff(nxt.nt * Cfg::kOutCols);
       b_base = b_base_of(nxt.e);
-      prologue(g, b_base);
     }
+    // The next tile's prologue (its first A slice and first NSB-1 B slices,
+    // kProCalls DMA pairs, in the order of prologue()) is issued spread over
+    // the first staging pass, one or two pairs per fragment group, so the
+    // wave's VALU and LDS work of the staging runs while the memory pipeline
+    // takes the DMA instructions (issued in one run, they held the wave for
+    // about as long as the TA needs for them). All of it precedes the
+    // output stores, as the next tile's first wait assumes.
+    constexpr int kProA = (NSA - 1) * (A_INS / 2), kProCalls = kProA + (NSB - 1) * (B_INS / 2);
+    auto pro_call = [&](int c) {
+      if (c < kProA) {
+        const int p = c / (A_INS / 2), i = 2 * (c % (A_INS / 2));
+        if (p < KT) dma2(i, p, g + p, b_base);
+      } else {
+        const int cc = c - kProA;
+        const int p = cc / (B_INS / 2), i = A_INS + 2 * (cc % (B_INS / 2));
+        if (p < KT) dma2(i, p, g + p, b_base);
+      }
+    };
+    constexpr int kGroups = SWIGLU ? Cfg::TM * (Cfg::TN / 2) : (Cfg::TM / 2) * Cfg::TN;
+    static_assert(SWIGLU || Cfg::TM % 2 == 0, "two staging passes for down");
+    auto pro_part = [&](int gi) {  // gi: fragment group of the first staging pass
+      if (!has_next) return;       // uniform
+#pragma unroll
+      for (int c = gi * kProCalls / kGroups; c < (gi + 1) * kProCalls / kGroups; ++c) pro_call(c);
+    };
     // Output staging: rows go through the two stages of the last slice,
     // region 0 = its A stage, region 1 = its B stage (32 KiB each), 16-byte
     // chunks XOR-swizzled by row; then whole rows are stored, 16 bytes per
@@ -1231,6 +1255,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
           constexpr int half = Cfg::TN / 2;
 #pragma unroll
           for (int tg = 0; tg < half; ++tg) {
+            pro_part(b * half + tg);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
               const int cc = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * elk;
@@ -1252,6 +1277,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         } else {
 #pragma unroll
           for (int tn = 0; tn < Cfg::TN; ++tn) {
+            if (ps == 0) pro_part(b * Cfg::TN + tn);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
               const int cc = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * elk;
