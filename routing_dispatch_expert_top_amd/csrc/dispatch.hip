@@ -39,26 +39,44 @@ struct BlockMasks {
   uint32_t emask[kMaxE * kWords];
   uint32_t rmask[kMaxG * kWords];
   int32_t place[kMaxE];
+  int32_t idx[kBlockTok * kMaxK];  // the block's routing choices
 };
 
 // Builds the block's bitmaps; returns the token's rank mask (0 if t >= T).
 // A choice's rank is place[expert], or rank_of[t * k + j] when rank_of is
-// given (replica-aware assignment).
+// given (replica-aware assignment). The block's choices are first staged in
+// LDS, all loads issued before the LDS is cleared, so the loop over a
+// token's choices waits for no memory. The loads are 16 bytes wide when
+// topk_idx is 16-byte aligned (a block's chunk starts 1024 k bytes in),
+// 4 bytes otherwise.
 __device__ uint32_t build_masks(BlockMasks& sm, const int32_t* __restrict__ topk_idx, int T,
                                 int E, int k, const int32_t* __restrict__ place,
                                 const int32_t* __restrict__ rank_of, int G) {
-  for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) sm.emask[i] = 0u;
-  for (int i = threadIdx.x; i < G * kWords; i += blockDim.x) sm.rmask[i] = 0u;
-  if (!rank_of)
-    for (int i = threadIdx.x; i < E; i += blockDim.x) sm.place[i] = place[i];
+  const int tb = blockIdx.x * kBlockTok;
+  const int n = min(kBlockTok, T - tb) * k;
+  {
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(topk_idx + (size_t)tb * k);
+    const int nv = (reinterpret_cast<uintptr_t>(topk_idx) & 15) ? 0 : n / 4;
+    u32x4 v[4];
+    int pl = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { const int i = threadIdx.x + j * kBlockTok; if (i < nv) v[j] = s4[i]; }
+    if (!rank_of && (int)threadIdx.x < E) pl = place[threadIdx.x];
+    for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) sm.emask[i] = 0u;
+    for (int i = threadIdx.x; i < G * kWords; i += blockDim.x) sm.rmask[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { const int i = threadIdx.x + j * kBlockTok; if (i < nv) reinterpret_cast<u32x4*>(sm.idx)[i] = v[j]; }
+    for (int i = 4 * nv + threadIdx.x; i < n; i += kBlockTok) sm.idx[i] = topk_idx[(size_t)tb * k + i];
+    if (!rank_of && (int)threadIdx.x < E) sm.place[threadIdx.x] = pl;
+  }
   __syncthreads();
-  const int t = blockIdx.x * kBlockTok + threadIdx.x;
+  const int t = tb + threadIdx.x;
   const int w = threadIdx.x >> 5;
   const uint32_t bit = 1u << (threadIdx.x & 31);
   uint32_t m = 0u;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
-      const int e = topk_idx[(size_t)t * k + j];
+      const int e = sm.idx[threadIdx.x * k + j];
       if (e < 0 || e >= E) continue;
       const int g = rank_of ? rank_of[(size_t)t * k + j] : sm.place[e];
       if (g < 0 || g >= G) continue;
@@ -119,9 +137,41 @@ struct ScanSmem {
   int32_t off[kMaxE + kMaxG];
 };
 
+// Up to kScanFast blocks with one key per thread: every count of the
+// thread's key is loaded in one round (all loads issued before any is used)
+// and kept in registers for the bases, instead of two walks in chunks.
+constexpr int kScanFast = 32;
+
 __device__ void scan_blocks(ScanSmem& sm, int32_t* __restrict__ cnt, int nblk, int E, int G,
                             int32_t* __restrict__ expert_off, int32_t* __restrict__ rank_off) {
   const int Q = E + G;
+  if (nblk <= kScanFast && Q <= (int)blockDim.x) {  // uniform
+    const int q = threadIdx.x;
+    int c[kScanFast];
+#pragma unroll
+    for (int i = 0; i < kScanFast; ++i)
+      c[i] = q < Q && i < nblk ? load_cnt(&cnt[(size_t)i * Q + q]) : 0;
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanFast; ++i) s += c[i];
+    if (q < Q) sm.tot[q] = s;
+    __syncthreads();
+    const int wave = threadIdx.x / kWave;
+    if (wave == 0) wave_excl_scan_256(sm.tot, sm.off, E, &expert_off[E]);
+    if (wave == 1) wave_excl_scan_256(sm.tot + E, sm.off + E, G, &rank_off[G]);
+    __syncthreads();
+    if (q < Q) {
+      int run = sm.off[q];
+      if (q < E) expert_off[q] = run;
+      else rank_off[q - E] = run;
+#pragma unroll
+      for (int i = 0; i < kScanFast; ++i) {
+        if (i < nblk) cnt[(size_t)i * Q + q] = run;
+        run += c[i];
+      }
+    }
+    return;
+  }
   for (int q = threadIdx.x; q < Q; q += blockDim.x) {
     int s = 0;
     for (int b0 = 0; b0 < nblk; b0 += kScanChunk) {

@@ -256,6 +256,41 @@ def test_layout_workspace_is_left_zero():
                                "slot_of"))
 
 
+SCAN_CASES = [(synth.with_shape(synth.workload(3), T=T), T) for T in (3000, 8192, 8193, 9000)] + [
+    (C("k3_E250", T=1001, d=64, E=250, k=3, F=64, G=10, dtype="bf16", clusters=10), 1001)]
+
+
+@pytest.mark.parametrize("w,T", SCAN_CASES, ids=[f"{w.name}-T{T}" for w, T in SCAN_CASES])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_layout_scan_paths_and_unaligned_choices(w, T, aligned):
+    """The count kernel's last block scans the per-block counts in one round
+    while there are at most 32 blocks of 256 tokens and E + G <= 256, in
+    chunks otherwise: T = 8192 is the last size on the one-round path, and
+    E + G = 260 takes the chunked one at any T. The block's choices are read
+    16 bytes at a time when topk_idx is 16-byte aligned and one word at a
+    time when it is not (here a view one element into a larger buffer); with
+    k = 3 a block's tail is read one word at a time either way. Every case
+    gives the oracle's layout bit for bit."""
+    inp = synth.make(w, place="contiguous", with_weights=False)
+    idx, _ = oracle.route(inp["logits"], w.k)
+    ref = oracle.layout(idx, w.E, inp["place"], w.G)
+    if aligned:
+        d_idx = dev(idx)
+    else:
+        buf = torch.zeros(idx.size + 1, dtype=torch.int32, device="cuda")
+        buf[1:] = dev(idx).reshape(-1)
+        d_idx = buf[1:].view(idx.shape)
+        assert d_idx.data_ptr() % 16 != 0
+    out = ops.moe_dispatch_layout(d_idx, w.E, dev(inp["place"]), w.G)
+    torch.cuda.synchronize()
+    R = int(out["rank_off"][w.G].item())
+    g = dict(rank_mask=host(out["rank_mask"]).view(np.uint32), rank_off=host(out["rank_off"]),
+             disp_token=host(out["disp_token"][:R]), expert_off=host(out["expert_off"]),
+             perm_row=host(out["perm_row"]), slot_of=host(out["slot_of"]))
+    compare_exact(g, ref, ("rank_mask", "rank_off", "disp_token", "expert_off", "perm_row",
+                           "slot_of"))
+
+
 def test_expert_workspace_is_left_zero_and_reused():
     """The persistent expert launches claim tiles from a queue in the caller's
     workspace and leave it zero-filled: two calls in a row on one workspace
