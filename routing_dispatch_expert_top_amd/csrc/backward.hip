@@ -415,18 +415,20 @@ __device__ __forceinline__ void silu_parts(float u, float& silu, float& dsilu) {
   dsilu = sg * (1.0f + u * (1.0f - sg));
 }
 
-// ---------------------------------------------------------------- fp32 SIMT GEMM
+// ---------------------------------------------------------------- fp32 MFMA GEMM
 
-// The same three GEMMs in fp32 with plain FMA (64 x 64 tiles, 16-deep K
-// slices, element loads through the mode's index map).
+// The same three GEMMs in fp32 on the fp32 matrix cores: 64 x 64 tiles,
+// 16-deep K slices staged in LDS K-major through the mode's index map, and
+// 4 wavefronts as 2 x 2, each accumulating a 32 x 32 block with
+// v_mfma_f32_32x32x2_f32 (lane l feeds row l % 32 at k = 2i + l / 32).
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(BwdArgs p, const float* A,
                                                            const float* W0, const float* W1,
                                                            float* C, const float* uv, float* duv,
                                                            const float* At, const float* Bt) {
   constexpr int BM = 64, BN = 64, BK = 16;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BN + 4];
+  __shared__ __align__(16) float As[BK][BM + 4];
+  __shared__ __align__(16) float Bs[BK][BN + 4];
   __shared__ Sched sc;
   int e, mt, nt, seg0, seg1, m0, c0, Kt;
   if (MODE != kWgrad) {
@@ -454,60 +456,79 @@ __global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(BwdArgs p, const floa
     c0 = nt * BN;
     Kt = seg1 - seg0;
   }
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < Kt; k0 += BK) {
-    for (int q = tid; q < BK * BM; q += 256) {
-      const int kk = q / BM, r = q % BM, k = k0 + kk;
-      float av = 0.f, bv = 0.f;
-      if (MODE != kWgrad) {
-        const int s = min(m0 + r, seg1 - 1);
-        av = A[(size_t)s * p.lda + k];
-        const int n = min(c0 + r, p.N0 - 1);
-        const float* w = k < p.ksplit ? W0 + (size_t)e * p.estride + (size_t)k * p.N0
-                                      : W1 + (size_t)e * p.estride + (size_t)(k - p.ksplit) * p.N0;
-        bv = w[n];
-      } else if (k < Kt) {
-        const int s = seg0 + k;
-        const int m = min(m0 + r, p.M0 - 1), n = min(c0 + r, p.N0 - 1);
-        av = At[(size_t)s * p.ldat + m];
-        bv = Bt[(size_t)(p.b_gather ? p.b_gather[s] : s) * p.ldbt + n];
-      }
-      As[kk][r] = av;
-      Bs[kk][r] = bv;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int kh = lane >> 5;
+  const int ar = (wave >> 1) * 32 + (lane & 31), bc = (wave & 1) * 32 + (lane & 31);
+  f32x16 acc = {};
+  // Each thread loads one 16-byte piece of each operand per slice. Data
+  // gradients: A rows [S][K] (row tid / 4, k 4 (tid % 4) ..) and the weight
+  // panel [K][N0] (k row tid / 16, n 4 (tid % 16) ..); weight gradients: At
+  // [S][M0] and Bt [S][N0] (slot k0 + tid / 16, m or n 4 (tid % 16) ..). M0,
+  // N0 and K are multiples of 64, so every piece is in bounds and aligned.
+  // The next slice's pieces are loaded before the current one's MFMAs.
+  const int r4 = tid >> 2, k4 = (tid & 3) * 4;  // data gradients: A piece
+  const int kr = tid >> 4, c4 = (tid & 15) * 4;  // the other pieces
+  const float* arow = nullptr;
+  if (MODE != kWgrad) arow = A + (size_t)min(m0 + r4, seg1 - 1) * p.lda;
+  auto load = [&](int k0, float4& av, float4& bv) {
+    const int k = k0 + kr;
+    if (MODE != kWgrad) {
+      av = *reinterpret_cast<const float4*>(arow + k0 + k4);
+      const float* w = k < p.ksplit ? W0 + (size_t)e * p.estride + (size_t)k * p.N0
+                                    : W1 + (size_t)e * p.estride + (size_t)(k - p.ksplit) * p.N0;
+      bv = *reinterpret_cast<const float4*>(w + c0 + c4);
+    } else if (k < Kt) {
+      const int s = seg0 + k;
+      av = *reinterpret_cast<const float4*>(At + (size_t)s * p.ldat + m0 + c4);
+      bv = *reinterpret_cast<const float4*>(Bt + (size_t)(p.b_gather ? p.b_gather[s] : s) * p.ldbt +
+                                            c0 + c4);
+    } else {
+      av = bv = float4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  float4 av, bv;
+  if (Kt > 0) load(0, av, bv);
+  for (int k0 = 0; k0 < Kt; k0 += BK) {
+    if (MODE != kWgrad) {
+      As[k4 + 0][r4] = av.x;
+      As[k4 + 1][r4] = av.y;
+      As[k4 + 2][r4] = av.z;
+      As[k4 + 3][r4] = av.w;
+    } else {
+      *reinterpret_cast<float4*>(&As[kr][c4]) = av;
+    }
+    *reinterpret_cast<float4*>(&Bs[kr][c4]) = bv;
     __syncthreads();
+    if (k0 + BK < Kt) load(k0 + BK, av, bv);
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(As[kk][ty * 4 + i], Bs[kk][tx * 4 + j], acc[i][j]);
+    for (int i = 0; i < BK / 2; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * i + kh][ar], Bs[2 * i + kh][bc], acc, 0, 0,
+                                                 0);
     __syncthreads();
   }
+  // Register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4 and
+  // column l % 32 of the wave's 32 x 32 block.
+  const int col = c0 + bc;
+  if (col >= p.N0) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + ty * 4 + i;
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + (wave >> 1) * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
     if (MODE != kWgrad ? row >= seg1 : row >= p.M0) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = c0 + tx * 4 + j;
-      if (col >= p.N0) continue;
-      if (MODE == kDgradPlain) {
-        C[(size_t)row * p.ldc + col] = acc[i][j];
-      } else if (MODE == kDgradSwiglu) {
-        const size_t o = (size_t)row * (2 * p.F) + col;
-        const float u = uv[o], v = uv[o + p.F];
-        float sl, ds;
-        silu_parts(u, sl, ds);
-        duv[o] = acc[i][j] * v * ds;
-        duv[o + p.F] = acc[i][j] * sl;
-      } else {
-        float* out = row < p.msplit
-                         ? p.O0 + ((size_t)e * p.msplit + row) * p.N0
-                         : p.O1 + ((size_t)e * (p.M0 - p.msplit) + (row - p.msplit)) * p.N0;
-        out[col] = acc[i][j];
-      }
+    if (MODE == kDgradPlain) {
+      C[(size_t)row * p.ldc + col] = acc[r];
+    } else if (MODE == kDgradSwiglu) {
+      const size_t o = (size_t)row * (2 * p.F) + col;
+      const float u = uv[o], v = uv[o + p.F];
+      float sl, ds;
+      silu_parts(u, sl, ds);
+      duv[o] = acc[r] * v * ds;
+      duv[o + p.F] = acc[r] * sl;
+    } else {
+      float* out = row < p.msplit
+                       ? p.O0 + ((size_t)e * p.msplit + row) * p.N0
+                       : p.O1 + ((size_t)e * (p.M0 - p.msplit) + (row - p.msplit)) * p.N0;
+      out[col] = acc[r];
     }
   }
 }

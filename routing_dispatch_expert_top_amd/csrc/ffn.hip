@@ -1340,8 +1340,17 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   }
 }
 
-// ---------------------------------------------------------------- fp32 SIMT
+// ---------------------------------------------------------------- fp32 MFMA
 
+// fp32 expert launches on the fp32 matrix cores (v_mfma_f32_32x32x2_f32).
+// A tile is 64 slots x 64 output columns; its 4 wavefronts are 2 x 2, each
+// owning 32 slots x 32 columns: for gate/up one 32 x 32 block of u and one
+// of v (the same columns of W_gate and W_up, so u and v of an element sit
+// in the same lane and register), for down one block of y. K runs in 32-wide
+// slices staged in LDS K-major (A as [k][slot], B as [k][weight row]), so
+// the operand a lane feeds each MFMA (row lane % 32, k = 2i + lane / 32) is
+// one 4-byte LDS read and a wave's read covers consecutive words. d and F
+// are multiples of 64, so K is a whole number of slices.
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
                                                        const int32_t* __restrict__ perm_row,
@@ -1350,89 +1359,103 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ B1, int K,
                                                        int N0, float* __restrict__ C,
                                                        float* __restrict__ UV) {
-  constexpr int BM = 64, BN = 64, BK = 16;
-  constexpr int kOutCols = SWIGLU ? BN / 2 : BN;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BN + 4];
+  constexpr int BM = 64, OC = 64, BK = 32;
+  constexpr int BR = SWIGLU ? 2 * OC : OC;  // weight rows per tile
+  // LDS row pitch in words: odd, so the 4 consecutive k a thread writes for
+  // one row, and the rows of neighbouring threads, fall in distinct banks
+  constexpr int PA = BM + 1, PB = BR + 1;
+  __shared__ float As[BK * PA];
+  __shared__ float Bs[BK * PB];
   __shared__ Sched sc;
   build_schedule(sc, expert_off, E, BM);
-  const int NT = (N0 + kOutCols - 1) / kOutCols;
+  const int NT = (N0 + OC - 1) / OC;
   const int tile = xcd_logical_tile(sc.mt_off[E] * NT);
   if (tile < 0) return;
   int e, nt, mt;
   decode_tile(sc, E, NT, tile, e, nt, mt);
   const int seg0 = expert_off[e], seg1 = expert_off[e + 1];
   const int m0 = seg0 + mt * BM;
-  const int c0 = nt * kOutCols;
+  const int c0 = nt * OC;
   const int tid = threadIdx.x;
-  const int ty = tid / 16, tx = tid % 16;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
 
-  // loads: 64 rows x 16 k per operand, 4 floats per thread
-  const int lr = tid / 4, lk = (tid % 4) * 4;
-  const int s = min(m0 + lr, seg1 - 1);
-  const float* arow = A + (size_t)(perm_row ? perm_row[s] : s) * K;
-  const float* bsrc;
-  {
-    int n;
-    const float* base;
-    if (SWIGLU) {
-      base = lr < BN / 2 ? B0 : B1;
-      n = c0 + (lr < BN / 2 ? lr : lr - BN / 2);
-    } else {
-      base = B0;
-      n = c0 + lr;
-    }
-    n = min(n, N0 - 1);
-    bsrc = base + ((size_t)e * N0 + n) * K;
-  }
-  // this thread's 4 B rows inside the tile
-  int bcol[4];
+  // Loads: 8 threads per row, each 4 consecutive k (one 16-byte load) of a
+  // 32-wide slice; A rows in 2 passes of 32, weight rows in BR / 32.
+  const int lr = tid >> 3, lk = (tid & 7) * 4;
+  const float* arow[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    bcol[j] = SWIGLU ? ((j < 2 ? 0 : BN / 2) + tx * 2 + (j & 1)) : tx * 4 + j;
+  for (int p = 0; p < 2; ++p) {
+    const int s = min(m0 + lr + 32 * p, seg1 - 1);  // rows past the segment: clamped, not stored
+    arow[p] = A + (size_t)(perm_row ? perm_row[s] : s) * K;
+  }
+  constexpr int BP = BR / 32;
+  const float* brow[BP];
+#pragma unroll
+  for (int p = 0; p < BP; ++p) {
+    const int r = lr + 32 * p;  // tile row: [0, OC) gate (or down) rows, [OC, 2 OC) up rows
+    const float* base = (SWIGLU && r >= OC) ? B1 : B0;
+    const int n = min(c0 + (r % OC), N0 - 1);
+    brow[p] = base + ((size_t)e * N0 + n) * K;
+  }
 
-  float acc[4][4] = {};
+  f32x16 acc0 = {}, acc1 = {};
+  const int ar = wm * 32 + (lane & 31), kh = lane >> 5;
+  const int br0 = wn * 32 + (lane & 31), br1 = br0 + OC;
+  // The next slice's pieces are loaded before the current one's MFMAs.
+  float4 av[2], bv[BP];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) av[p] = *reinterpret_cast<const float4*>(arow[p] + k0 + lk);
+#pragma unroll
+    for (int p = 0; p < BP; ++p) bv[p] = *reinterpret_cast<const float4*>(brow[p] + k0 + lk);
+  };
+  load(0);
   for (int k0 = 0; k0 < K; k0 += BK) {
-    const float4 av = *reinterpret_cast<const float4*>(arow + k0 + lk);
-    const float4 bv = *reinterpret_cast<const float4*>(bsrc + k0 + lk);
-    As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
-    Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
-    __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      float a[4], b[4];
+    for (int p = 0; p < 2; ++p) {
+      const int r = lr + 32 * p;
+      As[(lk + 0) * PA + r] = av[p].x;
+      As[(lk + 1) * PA + r] = av[p].y;
+      As[(lk + 2) * PA + r] = av[p].z;
+      As[(lk + 3) * PA + r] = av[p].w;
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][bcol[j]];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int p = 0; p < BP; ++p) {
+      const int r = lr + 32 * p;
+      Bs[(lk + 0) * PB + r] = bv[p].x;
+      Bs[(lk + 1) * PB + r] = bv[p].y;
+      Bs[(lk + 2) * PB + r] = bv[p].z;
+      Bs[(lk + 3) * PB + r] = bv[p].w;
     }
     __syncthreads();
-  }
+    if (k0 + BK < K) load(k0 + BK);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + ty * 4 + i;
+    for (int i = 0; i < BK / 2; ++i) {
+      const int kk = 2 * i + kh;
+      const float a = As[kk * PA + ar];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bs[kk * PB + br0], acc0, 0, 0, 0);
+      if (SWIGLU) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bs[kk * PB + br1], acc1, 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done reading the slice
+  }
+  // Register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4 and
+  // column l % 32 of the wave's 32 x 32 block.
+  const int col = c0 + wn * 32 + (lane & 31);
+  if (col >= N0) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
     if (row >= seg1) continue;
     if (SWIGLU) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = c0 + tx * 2 + j;
-        if (col >= N0) continue;
-        C[(size_t)row * N0 + col] = silu_mul(acc[i][j], acc[i][j + 2]);
-        if (UV) {
-          UV[(size_t)row * (2 * N0) + col] = acc[i][j];
-          UV[(size_t)row * (2 * N0) + N0 + col] = acc[i][j + 2];
-        }
+      C[(size_t)row * N0 + col] = silu_mul(acc0[r], acc1[r]);
+      if (UV) {
+        UV[(size_t)row * (2 * N0) + col] = acc0[r];
+        UV[(size_t)row * (2 * N0) + N0 + col] = acc1[r];
       }
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = c0 + tx * 4 + j;
-        if (col < N0) C[(size_t)row * N0 + col] = acc[i][j];
-      }
+      C[(size_t)row * N0 + col] = acc0[r];
     }
   }
 }
@@ -1564,7 +1587,7 @@ MOE_EXPORT moe_status moe_expert_gate_up(const void* x_disp, const int32_t* perm
                                    static_cast<uint16_t*>(h), static_cast<uint32_t*>(workspace),
                                    tiles, stream);
   }
-  const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 32);
+  const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 64);
   hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(tiles)), dim3(256), 0, stream,
                      static_cast<const float*>(x_disp), perm_row, expert_off, E,
                      static_cast<const float*>(w_gate), static_cast<const float*>(w_up), d, F,
@@ -1595,7 +1618,7 @@ MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t*
                        static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h),
                        static_cast<uint16_t*>(uv));
   } else {
-    const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 32);
+    const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 64);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(tiles)), dim3(256), 0, stream,
                        static_cast<const float*>(x_disp), perm_row, expert_off, E,
                        static_cast<const float*>(w_gate), static_cast<const float*>(w_up), d, F,
