@@ -206,10 +206,12 @@ __device__ __forceinline__ uint64_t dpp_min_step(uint64_t x) {
 // contiguous ranges of cap experts each, and a tile's work grows with its
 // expert's slot count, so the experts are dealt longest first to the
 // least-loaded XCD range with room left (ties: lower range); unused
-// positions hold -1.
+// positions hold -1. It also clears the weight-gradient launch's tile queue.
 __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ expert_off,
                                                           int E, int32_t* __restrict__ kseg,
-                                                          int32_t* __restrict__ eorder) {
+                                                          int32_t* __restrict__ eorder,
+                                                          uint32_t* __restrict__ queue) {
+  if (threadIdx.x < kQueueWords) queue[threadIdx.x] = 0u;
   __shared__ Sched sc;
   __shared__ int32_t sorted[kMaxE];
   __shared__ int32_t slen[kMaxE];
@@ -327,16 +329,18 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
 // Padded K length of the transposed operands for S slots over E experts.
 inline int64_t padded_k(int64_t S, int E) { return ceil_div(S + 63 * (int64_t)E, 64) * 64; }
 
-// Workspace of the weight-gradient path: kseg, then two transposed operands.
+// Workspace of the weight-gradient path: kseg, the expert order, the tile
+// queue, then two transposed operands.
 struct WgradWorkspace {
-  size_t kseg, eorder, at, bt, total;
+  size_t kseg, eorder, queue, at, bt, total;
 };
 inline WgradWorkspace wgrad_workspace(int64_t S, int E, int64_t rows_a, int64_t rows_b) {
   const int64_t ldk = padded_k(S, E);
   WgradWorkspace w;
   w.kseg = 0;
   w.eorder = ceil_div((E + 1) * 4, 256) * 256;
-  w.at = w.eorder + ceil_div(8 * ceil_div(E, 8) * 4, 256) * 256;
+  w.queue = w.eorder + ceil_div(8 * ceil_div(E, 8) * 4, 256) * 256;
+  w.at = w.queue + 256;
   w.bt = w.at + ceil_div(rows_a * ldk * 2, 256) * 256;
   w.total = w.bt + ceil_div(rows_b * ldk * 2, 256) * 256;
   return w;
@@ -353,24 +357,26 @@ bool bwd_bf16_fits(int64_t S, int E, int64_t k_dgrad, int64_t m0, int64_t n0) {
 // bf16 weight gradients through the forward's GEMM: transpose both operands
 // into expert-padded K-contiguous rows, then out[e] = at_e bt_e^T per
 // expert segment.
-void wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
-                const int32_t* b_gather, int N0, const int32_t* expert_off, int E, int64_t S,
-                int msplit, float* o0, float* o1, void* workspace, hipStream_t stream) {
+moe_status wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
+                      const int32_t* b_gather, int N0, const int32_t* expert_off, int E, int64_t S,
+                      int msplit, float* o0, float* o1, void* workspace, hipStream_t stream) {
   const int64_t ldk = padded_k(S, E);
   const WgradWorkspace ws = wgrad_workspace(S, E, M0, N0);
   char* w = static_cast<char*>(workspace);
   int32_t* kseg = reinterpret_cast<int32_t*>(w + ws.kseg);
   int32_t* eorder = reinterpret_cast<int32_t*>(w + ws.eorder);
+  uint32_t* queue = reinterpret_cast<uint32_t*>(w + ws.queue);
   uint16_t* at = reinterpret_cast<uint16_t*>(w + ws.at);
   uint16_t* bt = reinterpret_cast<uint16_t*>(w + ws.bt);
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_off, E, kseg,
-                     eorder);
+                     eorder, queue);
   const unsigned kt = (unsigned)(ldk / 64);
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)ceil_div(M0 / 64, kTrW)), dim3(256), 0,
                      stream, a, lda, nullptr, expert_off, kseg, E, M0, (int)ldk, at);
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)ceil_div(N0 / 64, kTrW)), dim3(256), 0,
                      stream, b, ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
-  launch_wgrad_bf16(at, bt, kseg, eorder, E, M0, N0, (int)ldk, msplit, o0, o1, stream);
+  return launch_wgrad_bf16(at, bt, kseg, eorder, E, M0, N0, (int)ldk, msplit, o0, o1, queue,
+                           stream);
 }
 
 // ---------------------------------------------------------------- fp32 GEMM descriptors
@@ -618,7 +624,8 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
   if (misaligned({dy, h, uv, w_down, duv, dw_down})) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
-    if (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F))
+    if (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F) ||
+        (uintptr_t)workspace % 16)
       return MOE_ERR_WORKSPACE;
     if (!bwd_bf16_fits(rows, E, d, d, F)) return MOE_ERR_UNSUPPORTED;
     // dh = dy W_down[e] (W_down[e] = d x F = K x N0), SwiGLU backward in the epilogue
@@ -627,9 +634,9 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
                         static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(w_down),
                         d, F, static_cast<const uint16_t*>(uv), static_cast<uint16_t*>(duv), stream);
     // dW_down[e] = dy^T h over the expert's slots
-    wgrad_bf16(static_cast<const uint16_t*>(dy), d, d, static_cast<const uint16_t*>(h), F, nullptr,
-               F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream);
-    return launch_status();
+    st = wgrad_bf16(static_cast<const uint16_t*>(dy), d, d, static_cast<const uint16_t*>(h), F,
+                    nullptr, F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream);
+    return st != MOE_OK ? st : launch_status();
   }
   BwdArgs p = {};
   p.expert_off = expert_off;
@@ -675,7 +682,8 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
   if (misaligned({duv, x_disp, w_gate, w_up, da, dw_gate, dw_up})) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
-    if (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F))
+    if (!workspace || workspace_bytes < moe_expert_bwd_workspace_bytes(T, E, k, d, F) ||
+        (uintptr_t)workspace % 16)
       return MOE_ERR_WORKSPACE;
     if (!bwd_bf16_fits(rows, E, 2 * F, 2 * F, d)) return MOE_ERR_UNSUPPORTED;
     // da = du W_gate[e] + dv W_up[e]: K = 2F (rows of W_gate[e], then of W_up[e]), N0 = d
@@ -684,10 +692,10 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
                         static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
                         F, d, nullptr, static_cast<uint16_t*>(da), stream);
     // [dW_gate; dW_up][e] = [du dv]^T a over the expert's slots, a = x_disp[perm_row[s]]
-    wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, 2 * F,
-               static_cast<const uint16_t*>(x_disp), d, perm_row, d, expert_off, E, rows, F,
-               dw_gate, dw_up, workspace, stream);
-    return launch_status();
+    st = wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, 2 * F,
+                    static_cast<const uint16_t*>(x_disp), d, perm_row, d, expert_off, E, rows, F,
+                    dw_gate, dw_up, workspace, stream);
+    return st != MOE_OK ? st : launch_status();
   }
   BwdArgs p = {};
   p.expert_off = expert_off;

@@ -99,15 +99,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // their misses cost the most. With NSA = 2 and NSB = 3 at 256 x 256 x 64 the
 // ring is exactly the 160 KiB of LDS of a gfx950 CU, so the tile schedule is
 // built inside the ring before the first DMA lands there.
-// WG (weight-gradient mode): Out[e][m][n] = sum over expert e's K segment
-// [kseg[e], kseg[e+1]) of A[m][k] B0[n][k] (A: M0 rows, B0: N0 rows, both of
-// row length K, each expert's segment a multiple of BK); every expert gets
-// ceil(M0/BM) x ceil(N0/BN) tiles, rows m < msplit go to O0 (msplit x N0 per
-// expert) and the others to O1, in fp32. An expert with an empty segment
-// writes zeros.
 // BT (transposed-weight mode, for the data gradients): B rows are K rows of
 // a [K][N0] panel (N contiguous; expert e's panel = ksplit x N0 elements of
-// B0 for k < ksplit, of B1 for k >= ksplit, with ksplit passed in msplit).
+// B0 for k < ksplit, of B1 for k >= ksplit).
 // Its slices are DMA-loaded raw (two 512-byte K rows per 1 KiB block, the
 // 16-byte chunk index XOR-ed with 2 (row & 3)) and each B fragment is two
 // ds_read_b64_tr_b16: inside a group of 16 lanes, lane j receives element
@@ -116,16 +110,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the 4 K values of column n0 + j (checked on the device).
 // SWB (SwiGLU backward epilogue): C = [du | dv] rows of 2 N0, from the tile
 // (dh) and the saved [u | v] rows in UV.
-template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU, bool WG = false,
-          bool BT = false, bool SWB = false>
+template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU, bool BT = false,
+          bool SWB = false>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
-    uint16_t* __restrict__ UV, const int32_t* __restrict__ kseg = nullptr, int M0 = 0,
-    int msplit = 0, float* __restrict__ O0 = nullptr, float* __restrict__ O1 = nullptr) {
-  static_assert(!(WG && SWIGLU), "weight-gradient mode has a plain epilogue");
-  static_assert(!BT || (!SWIGLU && !WG && BK == 64), "transposed-weight mode: data gradients");
+    uint16_t* __restrict__ UV, int ksplit = 0) {
+  static_assert(!BT || (!SWIGLU && BK == 64), "transposed-weight mode: data gradients");
   static_assert(!SWB || BT, "SwiGLU-backward epilogue belongs to the down data gradient");
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
@@ -144,42 +136,23 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   static_assert(BM * Cfg::kOutCols * 2 <= kRing * 16, "output tile fits the ring");
   static_assert(sizeof(TileSel) <= kRing * 16, "tile selection fits the ring");
 
-  int e = 0, nt = 0, mt = 0, sg0 = 0, sg1 = 0;
-  if (WG) {
-    // perm_row carries the expert order here: position p of the walk is
-    // expert perm_row[p] (-1: none), 8 ceil(E/8) positions, so each XCD's
-    // contiguous range of tiles covers whole positions
-    const int MT = (M0 + BM - 1) / BM, NT = (N0 + BN - 1) / BN;
-    const int tile = xcd_logical_tile(8 * ((E + 7) / 8) * MT * NT);
-    if (tile < 0) return;
-    const int pos = tile / (MT * NT);
-    e = perm_row[pos];
-    if (e < 0) return;  // uniform over the workgroup
-    const int rem = tile - pos * MT * NT;
-    mt = rem / NT;  // n-tiles inner: consecutive tiles share the A rows
-    nt = rem % NT;
-  } else {
+  int e = 0, nt = 0, mt = 0, seg0 = 0, send = 0;
+  {
     TileSel& ts = *reinterpret_cast<TileSel*>(ring);
     const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
-    if (!select_tile(ts, expert_off, E, BM, NT, e, nt, mt, sg0, sg1)) return;  // uniform
+    if (!select_tile(ts, expert_off, E, BM, NT, e, nt, mt, seg0, send)) return;  // uniform
     __syncthreads();  // every wave has its tile before the first DMA overwrites the selection
   }
-  // WG: rows are A's M0 rows (the row bound plays the segment end)
-  const int seg0 = WG ? 0 : sg0, send = WG ? M0 : sg1;
   // An expert's rows are split evenly, in whole 32-row bands, over its
   // ceil(rows / BM) m-tiles rather than as full tiles and a short last one:
   // the m-tiles of one weight panel then cost the same, start together and
   // stay in step, so each weight slice is fetched into the XCD's L2 once for
   // all of them (a short tile runs ahead and fetches the panel again).
-  int rows_per = BM;
-  if (!WG) {
-    const int me = send - seg0, nmt = (me + BM - 1) / BM;
-    rows_per = min(BM, ((me + nmt - 1) / nmt + 31) & ~31);
-  }
+  const int me = send - seg0, nmt = (me + BM - 1) / BM;
+  const int rows_per = min(BM, ((me + nmt - 1) / nmt + 31) & ~31);
   const int m0 = seg0 + mt * rows_per;
   const int seg1 = min(send, m0 + rows_per);  // end of this tile's rows
   const int c0 = nt * Cfg::kOutCols;
-  const int koff = WG ? kseg[e] : 0;  // first K column of the expert's segment
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -198,7 +171,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const int r = RPI * (wave * A_INS + i) + lane / CH;
     const int c = swz_ch<CH>(r, lane % CH) - r * CH;
     const int s = min(m0 + r, seg1 - 1);
-    const int src = (!WG && perm_row) ? perm_row[s] : s;  // WG: perm_row is the expert order
+    const int src = perm_row ? perm_row[s] : s;
     aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
   }
   const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
@@ -217,11 +190,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
     }
   }
-  const char* a_base = reinterpret_cast<const char*>(A) + (size_t)koff * 2 - kDmaBias;
-  const char* b_base =
-      WG ? reinterpret_cast<const char*>(B0) + (size_t)koff * 2 - kDmaBias
-         : reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow -
-               kDmaBias;  // expert e's panel
+  const char* a_base = reinterpret_cast<const char*>(A) - kDmaBias;
+  const char* b_base = reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow -
+                       kDmaBias;  // expert e's panel
   // DMA instructions i, i+1 (i even) of slice kt: i < A_INS fills A rows,
   // the rest B rows
   auto dma_ins2 = [&](int i, int kt) {
@@ -234,9 +205,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const char* base;
     if (BT && !is_a) {
       const int k0 = kt * BK;
-      const bool hi = k0 >= msplit;  // ksplit: uniform over the slice
+      const bool hi = k0 >= ksplit;  // uniform over the slice
       base = reinterpret_cast<const char*>(hi ? B1 : B0) +
-             ((size_t)e * msplit * N0 + (size_t)(hi ? k0 - msplit : k0) * N0) * 2 - kDmaBias;
+             ((size_t)e * ksplit * N0 + (size_t)(hi ? k0 - ksplit : k0) * N0) * 2 - kDmaBias;
     } else {
       base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
     }
@@ -302,26 +273,24 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = WG ? (kseg[e + 1] - koff) / BK : K / BK;
+  const int KT = K / BK;
   // Issue order (vmcnt counts in issue order): prologue A(0), .., A(NSA-2),
   // B(0), .., B(NSB-2); then the DMA issued during slice kt is A(kt+NSA-1)
   // followed by B(kt+NSB-1), into the stages slice kt-1 used. When slice kt
   // is needed, what was issued after the later of A(kt) and B(kt) may still
   // be in flight.
-  if (!WG || KT > 0) {
 #pragma unroll
-    for (int p = 0; p < NSA - 1; ++p)
-      if (p < KT) {
+  for (int p = 0; p < NSA - 1; ++p)
+    if (p < KT) {
 #pragma unroll
-        for (int i = 0; i < A_INS; i += 2) dma_ins2(i, p);
-      }
+      for (int i = 0; i < A_INS; i += 2) dma_ins2(i, p);
+    }
 #pragma unroll
-    for (int p = 0; p < NSB - 1; ++p)
-      if (p < KT) {
+  for (int p = 0; p < NSB - 1; ++p)
+    if (p < KT) {
 #pragma unroll
-        for (int i = A_INS; i < LPS; i += 2) dma_ins2(i, p);
-      }
-  }
+      for (int i = A_INS; i < LPS; i += 2) dma_ins2(i, p);
+    }
   constexpr int KS = BK / 16;  // MFMA k-steps per slice
   static_assert(KS % 2 == 0, "fragment double buffer parity");
   // Fragments are double-buffered (set (ks & 1) holds k-step ks). The last
@@ -483,9 +452,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     kstep(kCheck, 1, false, As[0], Bs[0], 0, KT, 0, 0);
   };
   static_assert(Cfg::TM <= 4, "band-count dispatch");
-  if (WG && KT == 0) {
-    // empty segment: nothing to load, the zero accumulators are written
-  } else switch (tm_live) {
+  switch (tm_live) {
     case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, (Cfg::TM >= 1 ? 1 : 0)>{}); break;
     case 2: k_loop(std::integral_constant<int, (Cfg::TM >= 2 ? 2 : 0)>{}); break;
@@ -584,26 +551,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
           const size_t o = (size_t)(m0 + r) * (2 * N0) + col;
           *reinterpret_cast<u32x4*>(C + o) = u32x4{du2[0], du2[1], du2[2], du2[3]};
           *reinterpret_cast<u32x4*>(C + o + N0) = u32x4{dv2[0], dv2[1], dv2[2], dv2[3]};
-        }
-      }
-    }
-  } else if (WG) {
-    // fp32 gradients: each lane's 4 consecutive columns are one 16-byte store
-#pragma unroll
-    for (int tm = 0; tm < Cfg::TM; ++tm) {
-      const int row = m0 + band_row(tm) + li;
-      if (row >= M0) continue;
-      float* orow = row < msplit ? O0 + ((size_t)e * msplit + row) * N0
-                                 : O1 + ((size_t)e * (M0 - msplit) + (row - msplit)) * N0;
-#pragma unroll
-      for (int tn = 0; tn < Cfg::TN; ++tn) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int col = c0 + wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
-          if (col >= N0) continue;
-          const f32x16& a = acc[tm][tn];
-          *reinterpret_cast<f32x4*>(orow + col) =
-              f32x4{a[4 * qd + 0], a[4 * qd + 1], a[4 * qd + 2], a[4 * qd + 3]};
         }
       }
     }
@@ -778,14 +725,28 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 // free.
 // The queue (8 counters and a finished-workgroup count) must be zero when a
 // launch starts; the last workgroup to finish sets it back to zero.
-constexpr int kQueueWords = 16;  // 8 XCD counters, the finish count, padding
+// WG (weight-gradient mode, for the backward): Out[e][m][n] = sum over
+// expert e's padded K segment [expert_off[e], expert_off[e+1]) of A[m][k]
+// B0[n][k] (A: M0 rows, B0: N0 rows, both K-contiguous rows of length K),
+// in fp32, rows m < msplit to O0 (msplit x N0 per expert) and the others to
+// O1. perm_row holds the expert walk: position p is expert perm_row[p] (-1:
+// none), 8 ceil(E/8) positions of ceil(M0/256) x ceil(N0/256) tiles each,
+// n-tiles inner; XCD x owns positions [x ceil(E/8), (x+1) ceil(E/8)). An
+// expert with an empty segment gets zeros. A tile's K loop length is its
+// expert's. The 256 KiB fp32 output goes through the two ring stages the
+// next tile's prologue leaves free, 64 rows a pass, and is stored in whole
+// 1 KiB rows (from the accumulator layout each store instruction would
+// touch 32 rows with 32 bytes each, and the CU's write path, not HBM, set
+// the pace).
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool WG = false>
 __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
-    uint32_t* __restrict__ queue) {
+    uint32_t* __restrict__ queue, int M0 = 0, int msplit = 0, float* __restrict__ O0 = nullptr,
+    float* __restrict__ O1 = nullptr) {
+  static_assert(!(WG && SWIGLU), "weight-gradient mode has a plain epilogue");
   constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, NSA = 2, NSB = 3;
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
@@ -806,14 +767,18 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int NT = (N0 + Cfg::kOutCols - 1) / Cfg::kOutCols;
-  const int KT = K / BK;
+  int KT = WG ? 0 : K / BK;  // weight gradients: the current tile's expert segment
   const uint32_t krow = (uint32_t)K * 2;
 
   // ---- expert schedule in registers: lane l holds the m-tile prefix of
   // experts 4l .. 4l+3 (two values per lane); the decode finds the lane by
   // a ballot and the expert inside it from scalar loads of expert_off
+  // Weight gradients: positions p = 0 .. 8 ceil(E/8) - 1 of the expert walk
+  // (expert perm_row[p], -1: none) times MT x NT tiles each, n-tiles inner;
+  // expert_off holds the padded K offsets of the experts' segments.
+  const int MT = WG ? (M0 + BM - 1) / BM : 1;
   int lane_mt = 0;
-  {
+  if (!WG) {
     int prev = expert_off[min(4 * lane, E)];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -830,7 +795,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     if (lane >= off) incl += o;
   }
   const int excl = incl - lane_mt;
-  const int total = __builtin_amdgcn_readlane(incl, kWave - 1) * NT;
+  const int total = WG ? 8 * ((E + 7) / 8) * MT * NT : __builtin_amdgcn_readlane(incl, kWave - 1) * NT;
 
   const int xcd = blockIdx.x % kXcd;
   const int S = gridDim.x / kXcd;  // workgroups per XCD (the grid is a multiple of 8)
@@ -843,6 +808,15 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   };
   auto decode = [&](int j) {
     const int n = xcd * q + j;
+    if (WG) {
+      const int pos = n / (MT * NT), rem = n - pos * MT * NT;
+      Tile t{perm_row[pos], rem % NT, rem / NT, 0, 0};
+      if (t.e >= 0) {
+        t.seg0 = expert_off[t.e];  // the expert's K segment
+        t.seg1 = expert_off[t.e + 1];
+      }
+      return t;
+    }
     const uint64_t bal = __ballot(incl * NT > n);
     const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)bal) - 1);
     int first = __builtin_amdgcn_readlane(excl, L);
@@ -899,6 +873,11 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   // ceil(rows / BM) m-tiles, so the m-tiles of one weight panel cost the
   // same and stay in step.
   auto tile_rows = [&](const Tile& t, int& m0, int& m1) {
+    if (WG) {  // rows of A (the weight gradient's rows)
+      m0 = t.mt * BM;
+      m1 = min(M0, m0 + BM);
+      return;
+    }
     const int me = t.seg1 - t.seg0, nmt = (me + BM - 1) / BM;
     const int rows_per = min(BM, ((me + nmt - 1) / nmt + 31) & ~31);
     m0 = t.seg0 + t.mt * rows_per;
@@ -924,6 +903,16 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
     }
   };
+  auto set_aoff_rows = [&](int m0, int m1) {  // weight gradients: A rows m0 .. m1-1, in order
+    const int ln = opaque_tid() & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = RPI * (wave * A_INS + i) + ln / CH;
+      const int c = swz_ch<CH>(r, ln % CH) - r * CH;
+      const int src = min(m0 + r, m1 - 1);
+      aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
+    }
+  };
   const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
   auto set_boff = [&](int c0) {
     const int ln = opaque_tid() & (kWave - 1);
@@ -939,6 +928,12 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   auto b_base_of = [&](int e) {
     return reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow - kDmaBias;
   };
+  // weight gradients: both operands start at the expert's K offset
+  auto wg_bases = [&](const Tile& t, const char*& bb) {
+    a_base = reinterpret_cast<const char*>(A) + (size_t)t.seg0 * 2 - kDmaBias;
+    bb = reinterpret_cast<const char*>(B0) + (size_t)t.seg0 * 2 - kDmaBias;
+  };
+  auto wg_kt = [&](const Tile& t) { return t.e >= 0 ? (t.seg1 - t.seg0) / BK : 0; };
   // DMA instructions i, i+1 (i even) of K slice kt into ring slot gs
   // (slots count slices across tiles: slice kt of a tile starting at slot g
   // goes to stA(g + kt), stB(g + kt))
@@ -956,6 +951,20 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     else dma_pair<2048>(v0, v1, base, m0v);
   };
   // first A slice and first NSB-1 B slices of a tile starting at slot g
+  // Weight gradients: A(0), B(0), B(1) of a tile starting at slot g (its
+  // A(1) and B(2) stages stage the previous tile's output meanwhile).
+  auto prologue_wg = [&](int g, const char* b_base, int kt_n) {
+    if (kt_n > 0) {
+#pragma unroll
+      for (int i = 0; i < A_INS; i += 2) dma2(i, 0, g, b_base);
+#pragma unroll
+      for (int p = 0; p < NSB - 1; ++p)
+        if (p < kt_n) {
+#pragma unroll
+          for (int i = A_INS; i < LPS; i += 2) dma2(i, p, g + p, b_base);
+        }
+    }
+  };
   auto prologue = [&](int g, const char* b_base) {
 #pragma unroll
     for (int p = 0; p < NSA - 1; ++p)
@@ -1003,10 +1012,17 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   if (cur_j < qx) {
     cur = decode(cur_j);
     tile_rows(cur, cm0, cm1);
-    set_aoff(load_rows(cm0, cm1));
     set_boff(cur.nt * Cfg::kOutCols);
-    b_base = b_base_of(cur.e);
-    prologue(0, b_base);
+    if (WG) {
+      set_aoff_rows(cm0, cm1);
+      wg_bases(cur, b_base);
+      KT = wg_kt(cur);
+      prologue_wg(0, b_base, KT);
+    } else {
+      set_aoff(load_rows(cm0, cm1));
+      b_base = b_base_of(cur.e);
+      prologue(0, b_base);
+    }
   }
   int pend_st = 0;  // store instructions of the previous epilogue (per thread, uniform)
   while (cur_j < qx) {
@@ -1015,7 +1031,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     if (has_next) {
       nxt = decode(nxt_j);
       tile_rows(nxt, nm0, nm1);
-      nsrc = load_rows(nm0, nm1);  // consumed in this tile's epilogue
+      if (!WG) nsrc = load_rows(nm0, nm1);  // consumed in this tile's epilogue
       // claim tile i+2 now; its value is read in the epilogue, after the K
       // loop has waited for every load (so reading it costs no extra wait)
       if (tid == 0) claim = (int)atomicAdd(&queue[xcd], 1u);
@@ -1059,6 +1075,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
             if ((NM > 0 ? qd * NM / np : 0) != jm) continue;
             const int i = lo + 2 * qd;
             const int nx = i < A_INS ? kt + NSA - 1 : kt + NSB - 1;
+            // weight gradients: slice 0's share (A(1), B(2)) came with the prologue
             if (!CHK || nx < KT) dma2(i, nx, g + nx, b_base);
           }
         };
@@ -1111,6 +1128,26 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         constexpr int kSteady = (NSB > NSA ? B_INS : 0) + (NSA - 2) * (A_INS + B_INS);
         constexpr int kFirst = (NSB - 2) * B_INS;
         static_assert(kSteady < 64 && kFirst + kMaxPendSt < 64, "vmcnt range");
+        if (WG) {
+          // Issue order at a tile's start: A(0), B(0), B(1) (if it exists),
+          // the previous tile's pend_st stores, the claim. A full tile's
+          // stores (kWgSt) alone outnumber the 63 a wait can leave in flight,
+          // so waiting for 63 covers A(0) and B(0); otherwise only the loads
+          // are counted. From slice 1 on, as in the forward.
+          constexpr int kWgSt = Cfg::TM * Cfg::TN * 4;
+          static_assert(kWgSt >= 63, "weight-gradient waits");
+          if (kt == 0) {
+            if (pend_st >= kWgSt) MOE_WAIT_VMCNT(63);
+            else if (KT > 1) MOE_WAIT_VMCNT(B_INS);
+            else MOE_WAIT_VMCNT(0);
+          } else if (kt >= NSA - 1 && kt + NSB - 2 < KT) {
+            MOE_WAIT_VMCNT(kSteady);
+          } else {
+            MOE_WAIT_VMCNT(0);
+          }
+          wg_barrier();
+          return;
+        }
         if (kt == 0 && NSB - 2 < KT) {
           if (pend_st == 2 * kStPass) MOE_WAIT_VMCNT(kFirst + 2 * kStPass);
           else if (pend_st == kStPass) MOE_WAIT_VMCNT(kFirst + kStPass);
@@ -1154,7 +1191,9 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       kstep(kCheck, 1, false, stA(g), stB(g), 0, KT, 0, 0);
     };
     static_assert(Cfg::TM <= 4, "band-count dispatch");
-    switch (tm_live) {
+    if (WG && KT == 0) {
+      // an expert without slots (zero gradients) or an unused position
+    } else switch (tm_live) {
       case 0: k_loop(std::integral_constant<int, 0>{}); break;
       case 1: k_loop(std::integral_constant<int, 1>{}); break;
       case 2: k_loop(std::integral_constant<int, 2>{}); break;
@@ -1174,6 +1213,82 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const int claim_s = __builtin_amdgcn_readfirstlane(claim);
     const int gl = g + KT - 1;  // ring slot of the last slice: its stages stage the output
     g += KT;
+    if constexpr (WG) {
+      char* const rb = reinterpret_cast<char*>(ring);
+      int claimed = 0, kt_n = 0;
+      if (has_next) {
+        // hand the claim (tile i+2) to every wave before the ring is refilled
+        if (tid == 0) *reinterpret_cast<int*>(rb) = claim_s;
+        wg_barrier();
+        claimed = *reinterpret_cast<const int*>(rb);
+        MOE_WAIT_LGKM0();
+        wg_barrier();
+        set_aoff_rows(nm0, nm1);
+        set_boff(nxt.nt * Cfg::kOutCols);
+        wg_bases(nxt, b_base);
+        kt_n = wg_kt(nxt);
+        prologue_wg(g, b_base, kt_n);
+      }
+      // fp32 gradient rows through the two ring stages the prologue left
+      // free (32 rows each), four passes of 64 tile rows: each wave writes
+      // its band's 16-byte pieces (chunk index XOR-ed with the row), then
+      // every wave stores whole 1 KiB rows, one per instruction.
+      pend_st = 0;
+      if (cur.e >= 0) {
+        const int etid = opaque_tid();
+        const int eli = etid & 31, elk = (etid >> 5) & 1;
+        const int ln = etid & 63;
+        const int n0e = opaque_s(N0);
+        u32x4* const rg0 = stA(g + 1);
+        u32x4* const rg1 = stB(g + 2);
+#pragma unroll
+        for (int ps = 0; ps < Cfg::TM; ++ps) {
+          if (cm0 + 64 * ps >= cm1) break;  // uniform
+          if (ps) wg_barrier();  // the previous pass has been read out
+          u32x4* wr = (wm ? rg1 : rg0) + eli * 64;
+#pragma unroll
+          for (int tn = 0; tn < Cfg::TN; ++tn) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              f32x4 v;
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) v[e4] = acc_read(acc[ps][tn][4 * qd + e4]);
+              const int ch = wn * 32 + tn * 8 + 2 * qd + elk;
+              wr[ch ^ eli] = __builtin_bit_cast(u32x4, v);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          MOE_WAIT_LGKM0();
+          wg_barrier();
+          const bool colok = 4 * ln < n0e - c0;
+#pragma unroll
+          for (int i0 = 0; i0 < 16; i0 += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = wave + 4 * (i0 + i);
+              v[i] = (r < 32 ? rg0 : rg1)[(r & 31) * 64 + (ln ^ (r & 31))];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int row = cm0 + 64 * ps + wave + 4 * (i0 + i);
+              float* orow = row < msplit ? O0 + ((size_t)cur.e * msplit + row) * n0e
+                                         : O1 + ((size_t)cur.e * (M0 - msplit) + (row - msplit)) * n0e;
+              if (colok) *reinterpret_cast<u32x4*>(orow + c0 + 4 * ln) = v[i];
+            }
+          }
+          pend_st += 16;
+        }
+      }
+      if (!has_next) break;  // uniform
+      cur = nxt;
+      cm0 = nm0;
+      cm1 = nm1;
+      KT = kt_n;
+      cur_j = nxt_j;
+      nxt_j = 2 * S + __builtin_amdgcn_readfirstlane(claimed);
+      continue;
+    }
     if (has_next) {
       // every DMA of this tile has landed (its last slice waited for all),
       // so the row indices loaded during the K loop are in too
@@ -1538,24 +1653,26 @@ void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_of
                        const uint16_t* uv, uint16_t* c, hipStream_t stream) {
   const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(N0, kBN);
   if (uv)
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, false, true, true>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true, true>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, a, nullptr,
-                       expert_off, E, w0, w1, K, N0, c, const_cast<uint16_t*>(uv), nullptr, 0,
-                       ksplit, nullptr, nullptr);
+                       expert_off, E, w0, w1, K, N0, c, const_cast<uint16_t*>(uv), ksplit);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, false, true, false>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true, false>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, a, nullptr,
-                       expert_off, E, w0, w1, K, N0, c, nullptr, nullptr, 0, ksplit, nullptr,
-                       nullptr);
+                       expert_off, E, w0, w1, K, N0, c, nullptr, ksplit);
 }
 
-void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
-                       const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
-                       float* o0, float* o1, hipStream_t stream) {
+moe_status launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
+                             const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
+                             float* o0, float* o1, uint32_t* queue, hipStream_t stream) {
   const int64_t tiles = 8 * ceil_div(E, 8) * ceil_div(M0, kBM) * ceil_div(N0, kBN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true>),
-                     dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, at, eorder,
-                     nullptr, E, bt, nullptr, ldk, N0, nullptr, nullptr, kseg, M0, msplit, o0, o1);
+  const int cus = cu_count();
+  if (cus <= 0) return MOE_ERR_DEVICE;
+  const int S = (int)std::max<int64_t>(1, std::min<int64_t>(cus / kXcd, tiles / kXcd));
+  hipLaunchKernelGGL((ffn_persistent_kernel<false, true>), dim3(kXcd * S), dim3(256), 0, stream,
+                     at, eorder, kseg, E, bt, nullptr, ldk, N0, nullptr, queue, M0, msplit, o0,
+                     o1);
+  return launch_status();
 }
 
 }  // namespace moe

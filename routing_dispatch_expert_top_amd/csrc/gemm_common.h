@@ -16,6 +16,9 @@ namespace {
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 constexpr int kXcd = 8;  // MI355X: workgroups go round-robin over 8 XCDs
+// Tile queue of the persistent grouped GEMMs: 8 XCD counters, the finish
+// count, padding. Zero when a launch starts; the launch leaves it zero.
+constexpr int kQueueWords = 16;
 
 // Per-workgroup tile schedule: prefix of M-tiles per expert in LDS.
 struct Sched {

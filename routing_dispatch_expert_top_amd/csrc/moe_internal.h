@@ -67,9 +67,10 @@ void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_of
                        const uint16_t* uv, uint16_t* c, hipStream_t stream);
 bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk);
 // eorder [8 * ceil(E/8)]: expert at each position of the tile walk (-1: none);
-// XCD x takes positions [x ceil(E/8), (x+1) ceil(E/8)).
-void launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
-                       const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
-                       float* o0, float* o1, hipStream_t stream);
+// XCD x takes positions [x ceil(E/8), (x+1) ceil(E/8)). A persistent launch:
+// queue (16 words) must be zero when it starts and is left zero.
+moe_status launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
+                             const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
+                             float* o0, float* o1, uint32_t* queue, hipStream_t stream);
 
 }  // namespace moe
