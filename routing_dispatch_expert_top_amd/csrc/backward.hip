@@ -330,18 +330,17 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
 inline int64_t padded_k(int64_t S, int E) { return ceil_div(S + 63 * (int64_t)E, 64) * 64; }
 
 // Workspace of the weight-gradient path: kseg, the expert order, the tile
-// queue, then two transposed operands.
+// queue, then the transposed second operand.
 struct WgradWorkspace {
-  size_t kseg, eorder, queue, at, bt, total;
+  size_t kseg, eorder, queue, bt, total;
 };
-inline WgradWorkspace wgrad_workspace(int64_t S, int E, int64_t rows_a, int64_t rows_b) {
+inline WgradWorkspace wgrad_workspace(int64_t S, int E, int64_t rows_b) {
   const int64_t ldk = padded_k(S, E);
   WgradWorkspace w;
   w.kseg = 0;
   w.eorder = ceil_div((E + 1) * 4, 256) * 256;
   w.queue = w.eorder + ceil_div(8 * ceil_div(E, 8) * 4, 256) * 256;
-  w.at = w.queue + 256;
-  w.bt = w.at + ceil_div(rows_a * ldk * 2, 256) * 256;
+  w.bt = w.queue + 256;
   w.total = w.bt + ceil_div(rows_b * ldk * 2, 256) * 256;
   return w;
 }
@@ -354,29 +353,26 @@ bool bwd_bf16_fits(int64_t S, int E, int64_t k_dgrad, int64_t m0, int64_t n0) {
          ldk < (int64_t(1) << 31);
 }
 
-// bf16 weight gradients through the forward's GEMM: transpose both operands
-// into expert-padded K-contiguous rows, then out[e] = at_e bt_e^T per
-// expert segment.
-moe_status wgrad_bf16(const uint16_t* a, int lda, int M0, const uint16_t* b, int ldb,
+// bf16 weight gradients through the forward's persistent GEMM: transpose b
+// into expert-padded K-contiguous rows (zero past each expert's slots), then
+// out[e] = a_e^T bt_e^T per expert segment, a read as it lies ([slots][M0]).
+moe_status wgrad_bf16(const uint16_t* a, int M0, const uint16_t* b, int ldb,
                       const int32_t* b_gather, int N0, const int32_t* expert_off, int E, int64_t S,
                       int msplit, float* o0, float* o1, void* workspace, hipStream_t stream) {
   const int64_t ldk = padded_k(S, E);
-  const WgradWorkspace ws = wgrad_workspace(S, E, M0, N0);
+  const WgradWorkspace ws = wgrad_workspace(S, E, N0);
   char* w = static_cast<char*>(workspace);
   int32_t* kseg = reinterpret_cast<int32_t*>(w + ws.kseg);
   int32_t* eorder = reinterpret_cast<int32_t*>(w + ws.eorder);
   uint32_t* queue = reinterpret_cast<uint32_t*>(w + ws.queue);
-  uint16_t* at = reinterpret_cast<uint16_t*>(w + ws.at);
   uint16_t* bt = reinterpret_cast<uint16_t*>(w + ws.bt);
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_off, E, kseg,
                      eorder, queue);
   const unsigned kt = (unsigned)(ldk / 64);
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)ceil_div(M0 / 64, kTrW)), dim3(256), 0,
-                     stream, a, lda, nullptr, expert_off, kseg, E, M0, (int)ldk, at);
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(kt, (unsigned)ceil_div(N0 / 64, kTrW)), dim3(256), 0,
                      stream, b, ldb, b_gather, expert_off, kseg, E, N0, (int)ldk, bt);
-  return launch_wgrad_bf16(at, bt, kseg, eorder, E, M0, N0, (int)ldk, msplit, o0, o1, queue,
-                           stream);
+  return launch_wgrad_bf16(a, bt, expert_off, kseg, eorder, E, M0, N0, (int)ldk, msplit, o0, o1,
+                           queue, stream);
 }
 
 // ---------------------------------------------------------------- fp32 GEMM descriptors
@@ -606,8 +602,8 @@ MOE_EXPORT size_t moe_expert_bwd_workspace_bytes(int32_t T, int32_t E, int32_t k
                                                  int32_t F) {
   if (T < 0 || E < 1 || k < 1 || d < 1 || F < 1) return 0;
   const int64_t S = (int64_t)T * k;
-  const size_t a = wgrad_workspace(S, E, d, F).total;      // down: dy^T, h^T
-  const size_t b = wgrad_workspace(S, E, 2 * F, d).total;  // gate/up: [du dv]^T, a^T
+  const size_t a = wgrad_workspace(S, E, F).total;  // down: h^T
+  const size_t b = wgrad_workspace(S, E, d).total;  // gate/up: gathered a^T
   return std::max(a, b);
 }
 
@@ -634,7 +630,7 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
                         static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(w_down),
                         d, F, static_cast<const uint16_t*>(uv), static_cast<uint16_t*>(duv), stream);
     // dW_down[e] = dy^T h over the expert's slots
-    st = wgrad_bf16(static_cast<const uint16_t*>(dy), d, d, static_cast<const uint16_t*>(h), F,
+    st = wgrad_bf16(static_cast<const uint16_t*>(dy), d, static_cast<const uint16_t*>(h), F,
                     nullptr, F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream);
     return st != MOE_OK ? st : launch_status();
   }
@@ -692,9 +688,8 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
                         static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
                         F, d, nullptr, static_cast<uint16_t*>(da), stream);
     // [dW_gate; dW_up][e] = [du dv]^T a over the expert's slots, a = x_disp[perm_row[s]]
-    st = wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, 2 * F,
-                    static_cast<const uint16_t*>(x_disp), d, perm_row, d, expert_off, E, rows, F,
-                    dw_gate, dw_up, workspace, stream);
+    st = wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, static_cast<const uint16_t*>(x_disp),
+                    d, perm_row, d, expert_off, E, rows, F, dw_gate, dw_up, workspace, stream);
     return st != MOE_OK ? st : launch_status();
   }
   BwdArgs p = {};

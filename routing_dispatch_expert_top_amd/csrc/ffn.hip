@@ -726,10 +726,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 // The queue (8 counters and a finished-workgroup count) must be zero when a
 // launch starts; the last workgroup to finish sets it back to zero.
 // WG (weight-gradient mode, for the backward): Out[e][m][n] = sum over
-// expert e's padded K segment [expert_off[e], expert_off[e+1]) of A[m][k]
-// B0[n][k] (A: M0 rows, B0: N0 rows, both K-contiguous rows of length K),
-// in fp32, rows m < msplit to O0 (msplit x N0 per expert) and the others to
-// O1. perm_row holds the expert walk: position p is expert perm_row[p] (-1:
+// the slots s of expert e, [expert_off[e], expert_off[e+1]), of A[s][m]
+// B0[n][kpad[e] + s - expert_off[e]]: A is [slots][M0] as it lies (M
+// contiguous), B0 the expert-padded transpose, N0 K-contiguous rows of
+// length K whose segment [kpad[e], kpad[e+1]) is zero past the expert's
+// slots; in fp32, rows m < msplit to O0 (msplit x N0 per expert) and the
+// others to O1. perm_row holds the expert walk: position p is expert perm_row[p] (-1:
 // none), 8 ceil(E/8) positions of ceil(M0/256) x ceil(N0/256) tiles each,
 // n-tiles inner; XCD x owns positions [x ceil(E/8), (x+1) ceil(E/8)). An
 // expert with an empty segment gets zeros. A tile's K loop length is its
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
     uint32_t* __restrict__ queue, int M0 = 0, int msplit = 0, float* __restrict__ O0 = nullptr,
-    float* __restrict__ O1 = nullptr) {
+    float* __restrict__ O1 = nullptr, const int32_t* __restrict__ kpad = nullptr) {
   static_assert(!(WG && SWIGLU), "weight-gradient mode has a plain epilogue");
   constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, NSA = 2, NSB = 3;
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
@@ -805,15 +807,18 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   // local tile j of this XCD -> expert, n-tile, m-tile, segment (all uniform)
   struct Tile {
     int e, nt, mt, seg0, seg1;
+    int kb, kt;  // weight gradients: first padded K column of B, K slices
   };
   auto decode = [&](int j) {
     const int n = xcd * q + j;
     if (WG) {
       const int pos = n / (MT * NT), rem = n - pos * MT * NT;
-      Tile t{perm_row[pos], rem % NT, rem / NT, 0, 0};
+      Tile t{perm_row[pos], rem % NT, rem / NT, 0, 0, 0, 0};
       if (t.e >= 0) {
-        t.seg0 = expert_off[t.e];  // the expert's K segment
+        t.seg0 = expert_off[t.e];  // the expert's slots (A rows)
         t.seg1 = expert_off[t.e + 1];
+        t.kb = kpad[t.e];  // and its padded columns of B
+        t.kt = (kpad[t.e + 1] - t.kb) / BK;
       }
       return t;
     }
@@ -852,15 +857,6 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     int t = tid;
     asm volatile("" : "+v"(t));
     return t;
-  };
-  // An accumulator element read into a VGPR where it is used: as an asm
-  // statement the read keeps its place, so the compiler neither copies every
-  // accumulator to VGPRs at the start of the epilogue nor moves them between
-  // AGPRs (which a pin of each fragment before its use costs).
-  auto acc_read = [](float a) {
-    float v;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-    return v;
   };
   // the same for uniform values (e.g. the row strides of the output stores)
   auto opaque_s = [&](int v) {
@@ -903,14 +899,20 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
     }
   };
-  auto set_aoff_rows = [&](int m0, int m1) {  // weight gradients: A rows m0 .. m1-1, in order
+  // Weight gradients: A is read as it lies, [slot][M0] (M contiguous), one
+  // K slice = 64 slot rows of the tile's 256 columns. DMA instruction i of
+  // the wave fills K rows 2 (wave A_INS + i) + {0, 1} of the stage, 512
+  // bytes each, lane l the physical 16-byte chunk l % 32 of row l / 32 with
+  // the logical chunk (l % 32) ^ 2 (row & 3) in it (as the data gradients'
+  // transposed weights); columns past M0 read the last 8 again.
+  auto set_aoff_raw = [&](int m0) {
     const int ln = opaque_tid() & (kWave - 1);
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-      const int r = RPI * (wave * A_INS + i) + ln / CH;
-      const int c = swz_ch<CH>(r, ln % CH) - r * CH;
-      const int src = min(m0 + r, m1 - 1);
-      aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
+      const int r = 2 * (wave * A_INS + i) + ln / 32;
+      const int c = (ln % 32) ^ (2 * (r & 3));
+      const int m = min(m0 + c * 8, M0 - 8);
+      aoff[i] = (uint32_t)(r * M0 + m) * 2u + kDmaBias - 1024u * (i & 3);
     }
   };
   const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
@@ -928,12 +930,19 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   auto b_base_of = [&](int e) {
     return reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow - kDmaBias;
   };
-  // weight gradients: both operands start at the expert's K offset
+  // Weight gradients: A from the expert's first slot row, B from its first
+  // padded column. In the last slice of an expert whose slot count is not a
+  // multiple of 64, rows past its last slot read that last slot's row again
+  // (B is zero there, and no other expert's rows enter its gradient).
+  int a_clamp_kt = -1, a_clamp_r = 0;  // that slice, and the last valid row in it
   auto wg_bases = [&](const Tile& t, const char*& bb) {
-    a_base = reinterpret_cast<const char*>(A) + (size_t)t.seg0 * 2 - kDmaBias;
-    bb = reinterpret_cast<const char*>(B0) + (size_t)t.seg0 * 2 - kDmaBias;
+    a_base = reinterpret_cast<const char*>(A) + (size_t)t.seg0 * M0 * 2 - kDmaBias;
+    bb = reinterpret_cast<const char*>(B0) + (size_t)t.kb * 2 - kDmaBias;
+    const int len = t.seg1 - t.seg0;
+    a_clamp_kt = (t.e >= 0 && len % BK) ? t.kt - 1 : -1;
+    a_clamp_r = len - 1 - (t.kt - 1) * BK;
   };
-  auto wg_kt = [&](const Tile& t) { return t.e >= 0 ? (t.seg1 - t.seg0) / BK : 0; };
+  auto wg_kt = [&](const Tile& t) { return t.e >= 0 ? t.kt : 0; };
   // DMA instructions i, i+1 (i even) of K slice kt into ring slot gs
   // (slots count slices across tiles: slice kt of a tile starting at slot g
   // goes to stA(g + kt), stB(g + kt))
@@ -945,8 +954,16 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(
         lds_addr(stage + RPI * (wave * ins + (ii & ~3)) * CH));
     const char* base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
-    const uint32_t v0 = is_a ? aoff[ii] : boff[ii];
-    const uint32_t v1 = is_a ? aoff[ii + 1] : boff[ii + 1];
+    uint32_t v0 = is_a ? aoff[ii] : boff[ii];
+    uint32_t v1 = is_a ? aoff[ii + 1] : boff[ii + 1];
+    if (WG && is_a) {
+      base = a_base + (size_t)kt * BK * M0 * 2;  // slice kt = slot rows 64 kt ..
+      if (kt == a_clamp_kt) {  // uniform
+        const int r = 2 * (wave * A_INS + ii) + (lane >> 5);
+        v0 -= (uint32_t)(max(0, r - a_clamp_r) * M0 * 2);
+        v1 -= (uint32_t)(max(0, r + 2 - a_clamp_r) * M0 * 2);
+      }
+    }
     if ((ii & 3) == 0) dma_pair<0>(v0, v1, base, m0v);
     else dma_pair<2048>(v0, v1, base, m0v);
   };
@@ -1000,6 +1017,29 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     return wn * Cfg::kWaveCols + tn * 32;
   };
   auto lane_off = [&](int ks) { return li * CH + ((2 * ks + lk) ^ xo); };
+  // Weight gradients: an A fragment from a raw [K][M] stage is two
+  // ds_read_b64_tr_b16 (K rows 16 ks + 8 (lane / 32) + 0..3 and + 4..7 of
+  // column band_row(tm) + lane % 32, as the data gradients' B fragments).
+  // fat0: this lane's byte offset of the first read of band 0 at k-step 0;
+  // band tm adds 128 tm bytes (the chunk XOR leaves the band bits alone),
+  // k-step ks 8192 ks, the second read 2048.
+  uint32_t fat0 = 0;
+  if (WG) {
+    const int g4 = lane >> 4, sl = lane & 15, kr = 8 * (g4 >> 1) + sl / 4;
+    const int col = wm * 32 + 16 * (g4 & 1) + 4 * (sl % 4);
+    fat0 = (uint32_t)(kr * 512 + (((col >> 3) ^ (2 * (kr & 3))) << 4) + (col & 7) * 2);
+  }
+  auto read_at = [&](const u32x4* as, int tm, int ks) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const char* b = reinterpret_cast<const char*>(as) + fat0 + tm * 128 + ks * 8192;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_void_t*)(b));
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_void_t*)(b + 2048));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  };
 
   // ---- the walk
   int cur_j = blockIdx.x / kXcd;  // slot s: local tiles s, s + S, then claims
@@ -1014,7 +1054,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     tile_rows(cur, cm0, cm1);
     set_boff(cur.nt * Cfg::kOutCols);
     if (WG) {
-      set_aoff_rows(cm0, cm1);
+      set_aoff_raw(cm0);
       wg_bases(cur, b_base);
       KT = wg_kt(cur);
       prologue_wg(0, b_base, KT);
@@ -1062,7 +1102,9 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         const u32x4* asl = as + a_uni + lo_;
         const u32x4* bsl = bs + lo_;
         auto read_frag = [&](int jr) {
-          if (jr < LIVE)
+          if (jr < LIVE && WG)
+            fa[set ^ 1][jr] = read_at(as, jr, ks_next);
+          else if (jr < LIVE)
             fa[set ^ 1][jr] = __builtin_bit_cast(bf16x8, asl[jr * WM * 32 * CH]);
           else
             fb[set ^ 1][jr - LIVE] = __builtin_bit_cast(bf16x8, bsl[b_row0(jr - LIVE) * CH]);
@@ -1100,7 +1142,8 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
 #pragma unroll
           for (int i = 0; i < NP; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (WG && i < LIVE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two tr reads
+            else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           if (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
           if (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
@@ -1112,7 +1155,8 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         const int lo_ = lane_off(0);
 #pragma unroll
         for (int tm = 0; tm < LIVE; ++tm)
-          fa[0][tm] = __builtin_bit_cast(bf16x8, as[a_uni + lo_ + tm * WM * 32 * CH]);
+          fa[0][tm] = WG ? read_at(as, tm, 0)
+                         : __builtin_bit_cast(bf16x8, as[a_uni + lo_ + tm * WM * 32 * CH]);
 #pragma unroll
         for (int tn = 0; tn < Cfg::TN; ++tn)
           fb[0][tn] = __builtin_bit_cast(bf16x8, bs[lo_ + b_row0(tn) * CH]);
@@ -1223,7 +1267,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         claimed = *reinterpret_cast<const int*>(rb);
         MOE_WAIT_LGKM0();
         wg_barrier();
-        set_aoff_rows(nm0, nm1);
+        set_aoff_raw(nm0);
         set_boff(nxt.nt * Cfg::kOutCols);
         wg_bases(nxt, b_base);
         kt_n = wg_kt(nxt);
@@ -1662,16 +1706,17 @@ void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_of
                        expert_off, E, w0, w1, K, N0, c, nullptr, ksplit);
 }
 
-moe_status launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
-                             const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
-                             float* o0, float* o1, uint32_t* queue, hipStream_t stream) {
+moe_status launch_wgrad_bf16(const uint16_t* a, const uint16_t* bt, const int32_t* expert_off,
+                             const int32_t* kseg, const int32_t* eorder, int E, int M0, int N0,
+                             int ldk, int msplit, float* o0, float* o1, uint32_t* queue,
+                             hipStream_t stream) {
   const int64_t tiles = 8 * ceil_div(E, 8) * ceil_div(M0, kBM) * ceil_div(N0, kBN);
   const int cus = cu_count();
   if (cus <= 0) return MOE_ERR_DEVICE;
   const int S = (int)std::max<int64_t>(1, std::min<int64_t>(cus / kXcd, tiles / kXcd));
   hipLaunchKernelGGL((ffn_persistent_kernel<false, true>), dim3(kXcd * S), dim3(256), 0, stream,
-                     at, eorder, kseg, E, bt, nullptr, ldk, N0, nullptr, queue, M0, msplit, o0,
-                     o1);
+                     a, eorder, expert_off, E, bt, nullptr, ldk, N0, nullptr, queue, M0, msplit, o0,
+                     o1, kseg);
   return launch_status();
 }
 

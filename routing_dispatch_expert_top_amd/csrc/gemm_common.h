@@ -15,6 +15,16 @@ namespace {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// An accumulator element read into a VGPR where it is used: as an asm
+// statement the read keeps its place, so the compiler neither copies every
+// accumulator to VGPRs at the start of an epilogue nor moves them between
+// AGPRs (which a pin of each fragment before its use costs).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 constexpr int kXcd = 8;  // MI355X: workgroups go round-robin over 8 XCDs
 // Tile queue of the persistent grouped GEMMs: 8 XCD counters, the finish
 // count, padding. Zero when a launch starts; the launch leaves it zero.

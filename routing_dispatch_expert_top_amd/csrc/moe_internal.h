@@ -53,10 +53,11 @@ inline int dtype_bytes(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Weight-gradient mode of the forward's bf16 grouped GEMM (ffn.hip):
-// out[e][m][n] = sum over expert e's K segment [kseg[e], kseg[e+1]) of
-// at[m][k] bt[n][k]; at is M0 x ldk, bt is N0 x ldk (bf16, K contiguous,
-// segments multiples of 64), fp32 output split at row msplit.
+// Weight-gradient mode of the forward's persistent bf16 grouped GEMM
+// (ffn.hip): out[e][m][n] = sum over the slots s of expert e of a[s][m]
+// bt[n][kseg[e] + s - expert_off[e]]; a is [slots][M0] (M contiguous), bt is
+// N0 x ldk (bf16, K contiguous, each expert's segment padded with zeros to a
+// multiple of 64), fp32 output split at row msplit.
 // Data-gradient mode (ffn.hip): c[s] = a[s] W[e] for the slots s of expert
 // e, W[e] = [K][N0] bf16 (rows k < ksplit from w0's panel e of ksplit x N0,
 // the rest from w1's); with uv, the epilogue applies the SwiGLU backward and
@@ -69,8 +70,9 @@ bool wgrad_offsets_fit(int64_t m0, int64_t n0, int64_t ldk);
 // eorder [8 * ceil(E/8)]: expert at each position of the tile walk (-1: none);
 // XCD x takes positions [x ceil(E/8), (x+1) ceil(E/8)). A persistent launch:
 // queue (16 words) must be zero when it starts and is left zero.
-moe_status launch_wgrad_bf16(const uint16_t* at, const uint16_t* bt, const int32_t* kseg,
-                             const int32_t* eorder, int E, int M0, int N0, int ldk, int msplit,
-                             float* o0, float* o1, uint32_t* queue, hipStream_t stream);
+moe_status launch_wgrad_bf16(const uint16_t* a, const uint16_t* bt, const int32_t* expert_off,
+                             const int32_t* kseg, const int32_t* eorder, int E, int M0, int N0,
+                             int ldk, int msplit, float* o0, float* o1, uint32_t* queue,
+                             hipStream_t stream);
 
 }  // namespace moe
