@@ -624,15 +624,17 @@ MOE_EXPORT moe_status moe_expert_down_bwd(const void* dy, const void* h, const v
         (uintptr_t)workspace % 16)
       return MOE_ERR_WORKSPACE;
     if (!bwd_bf16_fits(rows, E, d, d, F)) return MOE_ERR_UNSUPPORTED;
+    // dW_down[e] = dy^T h over the expert's slots (first: the data gradient's
+    // output, du dv, is what the next call reads, so it is written last)
+    st = wgrad_bf16(static_cast<const uint16_t*>(dy), d, static_cast<const uint16_t*>(h), F,
+                    nullptr, F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream);
+    if (st != MOE_OK) return st;
     // dh = dy W_down[e] (W_down[e] = d x F = K x N0), SwiGLU backward in the epilogue
     if (rows > 0)
       launch_dgrad_bf16(static_cast<const uint16_t*>(dy), rows, expert_off, E, d,
                         static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(w_down),
                         d, F, static_cast<const uint16_t*>(uv), static_cast<uint16_t*>(duv), stream);
-    // dW_down[e] = dy^T h over the expert's slots
-    st = wgrad_bf16(static_cast<const uint16_t*>(dy), d, static_cast<const uint16_t*>(h), F,
-                    nullptr, F, expert_off, E, rows, d, dw_down, dw_down, workspace, stream);
-    return st != MOE_OK ? st : launch_status();
+    return launch_status();
   }
   BwdArgs p = {};
   p.expert_off = expert_off;
@@ -682,15 +684,17 @@ MOE_EXPORT moe_status moe_expert_gate_up_bwd(const void* duv, const void* x_disp
         (uintptr_t)workspace % 16)
       return MOE_ERR_WORKSPACE;
     if (!bwd_bf16_fits(rows, E, 2 * F, 2 * F, d)) return MOE_ERR_UNSUPPORTED;
+    // [dW_gate; dW_up][e] = [du dv]^T a over the expert's slots, a = x_disp[perm_row[s]]
+    // (first: da, which the dispatch backward reads next, is written last)
+    st = wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, static_cast<const uint16_t*>(x_disp),
+                    d, perm_row, d, expert_off, E, rows, F, dw_gate, dw_up, workspace, stream);
+    if (st != MOE_OK) return st;
     // da = du W_gate[e] + dv W_up[e]: K = 2F (rows of W_gate[e], then of W_up[e]), N0 = d
     if (rows > 0)
       launch_dgrad_bf16(static_cast<const uint16_t*>(duv), rows, expert_off, E, 2 * F,
                         static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
                         F, d, nullptr, static_cast<uint16_t*>(da), stream);
-    // [dW_gate; dW_up][e] = [du dv]^T a over the expert's slots, a = x_disp[perm_row[s]]
-    st = wgrad_bf16(static_cast<const uint16_t*>(duv), 2 * F, static_cast<const uint16_t*>(x_disp),
-                    d, perm_row, d, expert_off, E, rows, F, dw_gate, dw_up, workspace, stream);
-    return st != MOE_OK ? st : launch_status();
+    return launch_status();
   }
   BwdArgs p = {};
   p.expert_off = expert_off;
