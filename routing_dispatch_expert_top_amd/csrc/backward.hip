@@ -13,17 +13,22 @@
 //   routing   dlogits[t, idx[t,j]] = g_j (dg_j - sum_i g_i dg_i), else 0
 //
 // gfx950 mapping of the two GEMM shapes (bf16), both on the forward's DMA
-// grouped GEMM (ffn.hip):
-//   data gradients: rows = an expert's slots; the weight panel is read as
-//     [K][N] (output dimension contiguous): its slices are DMA-loaded raw and
-//     the MFMA fragments come from gfx950's transposing LDS reads; the down
-//     data gradient applies the SwiGLU backward in its epilogue;
-//   weight gradients: the reduction runs over an expert's slots, so both
-//     operands are first transposed into K-contiguous rows with each
+// grouped GEMMs (ffn.hip):
+//   data gradients (one-tile kernel): rows = an expert's slots; the weight
+//     panel is read as [K][N] (output dimension contiguous): its slices are
+//     DMA-loaded raw and the MFMA fragments come from gfx950's transposing
+//     LDS reads; the down data gradient applies the SwiGLU backward in its
+//     epilogue;
+//   weight gradients (persistent kernel): the reduction runs over an
+//     expert's slots; the first operand (dy, or [du dv]) is read as it lies
+//     through the same transposing LDS reads, the second (h, or the
+//     gathered a) is first transposed into K-contiguous rows with each
 //     expert's slot range zero-padded to whole 64-wide K slices
-//     (transpose_pad_kernel, through LDS), and a weight-gradient mode of the
-//     same GEMM walks each expert's K segment, writing fp32.
-// fp32 uses plain LDS-tiled FMA kernels for every GEMM.
+//     (transpose_pad_kernel, through LDS); each expert's K segment is walked
+//     and the result written in fp32. Each expert call runs its weight
+//     gradient first, so the data gradient the next call reads is written
+//     last.
+// fp32 runs every GEMM on the fp32 matrix cores (gemm_bwd_f32_kernel).
 #include "moe_internal.h"
 #include "gemm_common.h"
 
