@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -297,11 +297,13 @@ moe_status moe_combine(const void* y, const int32_t* slot_of, const float* gates
  */
 
 /* Forward gate/up that also keeps the pre-activations for the backward:
- * uv [T*k, 2F] (dt): row s = [u_s | v_s] (u = W_gate a, v = W_up a). */
+ * uv [T*k, 2F] (dt): row s = [u_s | v_s] (u = W_gate a, v = W_up a).
+ * workspace as for moe_expert_gate_up. */
 moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t* perm_row,
                                    const int32_t* expert_off, int32_t T, int32_t E, int32_t k,
                                    int32_t d, int32_t F, const void* w_gate, const void* w_up,
-                                   moe_dtype dt, void* h, void* uv, hipStream_t stream);
+                                   moe_dtype dt, void* h, void* uv, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Combine backward: dy[slot_of[t*k+j]] = gates[t,j] * dout[t] (dt) and
  * dgates[t,j] = <dout[t], y[slot_of[t*k+j]]> (fp32 accumulation).
@@ -312,9 +314,10 @@ moe_status moe_combine_bwd(const void* dout, const void* y, const int32_t* slot_
                            void* dy, float* dgates, hipStream_t stream);
 
 /* Bytes of device workspace moe_expert_down_bwd and moe_expert_gate_up_bwd
- * need (host call, no GPU): in bf16 the weight gradients transpose their two
- * operands into expert-padded K-contiguous rows there, so the forward's
- * grouped GEMM computes them (about (2F + d) * (T*k + 64 E) * 2 bytes). */
+ * need (host call, no GPU): in bf16 the weight gradients transpose their
+ * second operand (h, or the gathered a) into expert-padded K-contiguous rows
+ * there and keep the persistent launch's tile queue (about
+ * max(F, d) * (T*k + 64 E) * 2 bytes). */
 size_t moe_expert_bwd_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t d, int32_t F);
 
 /* Down projection and SwiGLU backward, per expert e over its slots s:

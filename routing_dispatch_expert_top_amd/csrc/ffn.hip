@@ -99,9 +99,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // their misses cost the most. With NSA = 2 and NSB = 3 at 256 x 256 x 64 the
 // ring is exactly the 160 KiB of LDS of a gfx950 CU, so the tile schedule is
 // built inside the ring before the first DMA lands there.
-// BT (transposed-weight mode, for the data gradients): B rows are K rows of
-// a [K][N0] panel (N contiguous; expert e's panel = ksplit x N0 elements of
-// B0 for k < ksplit, of B1 for k >= ksplit).
+// The one-tile kernel computes the backward's data gradients: C[s] = A[s]
+// W[e] for the slots s of expert e, where the weight panel is read as
+// [K][N0] (N contiguous; expert e's panel = ksplit x N0 elements of B0 for
+// k < ksplit, of B1 for k >= ksplit).
 // Its slices are DMA-loaded raw (two 512-byte K rows per 1 KiB block, the
 // 16-byte chunk index XOR-ed with 2 (row & 3)) and each B fragment is two
 // ds_read_b64_tr_b16: inside a group of 16 lanes, lane j receives element
@@ -110,16 +111,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the 4 K values of column n0 + j (checked on the device).
 // SWB (SwiGLU backward epilogue): C = [du | dv] rows of 2 N0, from the tile
 // (dh) and the saved [u | v] rows in UV.
-template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWIGLU, bool BT = false,
-          bool SWB = false>
-__global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
+template <int BM, int BN, int BK, int WM, int WN, int NSA, int NSB, bool SWB = false>
+__global__ __launch_bounds__(WM* WN* kWave) void dgrad_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
     uint16_t* __restrict__ UV, int ksplit = 0) {
-  static_assert(!BT || (!SWIGLU && BK == 64), "transposed-weight mode: data gradients");
-  static_assert(!SWB || BT, "SwiGLU-backward epilogue belongs to the down data gradient");
-  using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
+  static_assert(BK == 64, "two 512-byte K rows per 1 KiB DMA block");
+  using Cfg = TileCfg<BM, BN, WM, WN, false>;
   constexpr int NW = WM * WN;
   constexpr int CH = BK / 8;           // 16-byte chunks per row of a K slice
   constexpr int RPI = 512 / BK;        // rows filled by one 1 KiB DMA instruction
@@ -163,7 +162,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   // its operand (INS = A_INS or B_INS), so a wave's blocks are contiguous
   // and groups of 4 share one M0 value (immediate offsets 0..3072).
   static_assert(A_INS % 2 == 0 && B_INS % 2 == 0 && (LPS / (BK / 16)) % 2 == 0, "DMA pairs");
-  static_assert(!SWIGLU || (BN / 2) % (B_INS * RPI) == 0, "a wave's B rows sit in one half");
   const uint32_t krow = (uint32_t)K * 2;  // bytes per operand row
   uint32_t aoff[A_INS], boff[B_INS];
 #pragma unroll
@@ -174,25 +172,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const int src = perm_row ? perm_row[s] : s;
     aoff[i] = (uint32_t)src * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
   }
-  const bool b_up = SWIGLU && wave * B_INS * RPI >= BN / 2;  // wave-uniform
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    if (BT) {
-      // block i of the wave = K rows 2 (wave B_INS + i) + {0, 1} of the slice
-      const int r = 2 * (wave * B_INS + i) + lane / 32;
-      const int c = (lane % 32) ^ (2 * (r & 3));  // logical chunk in this physical slot
-      const int n = min(c0 + c * 8, N0 - 8);
-      boff[i] = (uint32_t)(r * N0 + n) * 2u + kDmaBias - 1024u * (i & 3);
-    } else {
-      const int r = RPI * (wave * B_INS + i) + lane / CH;
-      const int c = swz_ch<CH>(r, lane % CH) - r * CH;
-      const int n = min(c0 + (b_up ? r - BN / 2 : r), N0 - 1);
-      boff[i] = (uint32_t)n * krow + (uint32_t)c * 16 + kDmaBias - 1024u * (i & 3);
-    }
+    // block i of the wave = K rows 2 (wave B_INS + i) + {0, 1} of the slice
+    const int r = 2 * (wave * B_INS + i) + lane / 32;
+    const int c = (lane % 32) ^ (2 * (r & 3));  // logical chunk in this physical slot
+    const int n = min(c0 + c * 8, N0 - 8);
+    boff[i] = (uint32_t)(r * N0 + n) * 2u + kDmaBias - 1024u * (i & 3);
   }
   const char* a_base = reinterpret_cast<const char*>(A) - kDmaBias;
-  const char* b_base = reinterpret_cast<const char*>(b_up ? B1 : B0) + (size_t)e * N0 * krow -
-                       kDmaBias;  // expert e's panel
   // DMA instructions i, i+1 (i even) of slice kt: i < A_INS fills A rows,
   // the rest B rows
   auto dma_ins2 = [&](int i, int kt) {
@@ -203,13 +191,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(
         lds_addr(stage + RPI * (wave * ins + (ii & ~3)) * CH));
     const char* base;
-    if (BT && !is_a) {
+    if (!is_a) {
       const int k0 = kt * BK;
       const bool hi = k0 >= ksplit;  // uniform over the slice
       base = reinterpret_cast<const char*>(hi ? B1 : B0) +
              ((size_t)e * ksplit * N0 + (size_t)(hi ? k0 - ksplit : k0) * N0) * 2 - kDmaBias;
     } else {
-      base = (is_a ? a_base : b_base) + (size_t)kt * (BK * 2);
+      base = a_base + (size_t)kt * (BK * 2);
     }
     const uint32_t v0 = is_a ? aoff[ii] : boff[ii];
     const uint32_t v1 = is_a ? aoff[ii + 1] : boff[ii + 1];
@@ -225,25 +213,14 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   // of them rather than all of its contiguous half of the tile.
   auto band_row = [&](int tm) { return (tm * WM + wm) * 32; };  // first tile row of band tm
   const int li = lane & 31, lk = lane >> 5;
-  int fa_row[Cfg::TM], fb_row[Cfg::TN];
+  int fa_row[Cfg::TM];
 #pragma unroll
   for (int tm = 0; tm < Cfg::TM; ++tm) fa_row[tm] = band_row(tm) + li;
-#pragma unroll
-  for (int tn = 0; tn < Cfg::TN; ++tn) {
-    int br;
-    if (SWIGLU) {
-      constexpr int half = Cfg::TN / 2;
-      br = (tn < half ? 0 : BN / 2) + wn * (Cfg::kWaveCols / 2) + (tn % half) * 32;
-    } else {
-      br = wn * Cfg::kWaveCols + tn * 32;
-    }
-    fb_row[tn] = br + li;
-  }
-  // BT: byte offset in a B stage of this lane's first transposed read of
+  // byte offset in a B stage of this lane's first transposed read of
   // fragment tn at k-step 0 (k-step ks adds 16 K rows = 8192 bytes, the
   // second read 4 K rows = 2048 bytes)
   uint32_t fbt_off[Cfg::TN];
-  if (BT) {
+  {
     const int g = lane >> 4, sl = lane & 15;
     const int kb = 8 * (g >> 1) + sl / 4;
 #pragma unroll
@@ -326,10 +303,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       auto read_frag = [&](int j) {
         if (j < LIVE)
           fa[set ^ 1][j] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[j], ch)]);
-        else if (BT)
-          fb[set ^ 1][j - LIVE] = read_bt(bs, j - LIVE, ks_next);
         else
-          fb[set ^ 1][j - LIVE] = __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[j - LIVE], ch)]);
+          fb[set ^ 1][j - LIVE] = read_bt(bs, j - LIVE, ks_next);
       };
       auto dma_at = [&](int j) {  // DMA pairs that go right after MFMA j
         const int np = nd / 2;
@@ -371,10 +346,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          if (BT && i >= LIVE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-          else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // DS read
+          if (i >= LIVE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+          else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
         }
-        constexpr int REM_B = BT ? (NR - (NP > LIVE ? NP : LIVE)) : 0;
+        constexpr int REM_B = NR - (NP > LIVE ? NP : LIVE);
         constexpr int REM_DS = (NR - NP) + (REM_B > 0 ? REM_B : 0);
         if (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
         if (REM_DS > 0) __builtin_amdgcn_sched_group_barrier(0x100, REM_DS, 0);
@@ -389,7 +364,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         fa[0][tm] = __builtin_bit_cast(bf16x8, as[swz_ch<CH>(fa_row[tm], ch)]);
 #pragma unroll
       for (int tn = 0; tn < Cfg::TN; ++tn)
-        fb[0][tn] = BT ? read_bt(bs, tn, 0) : __builtin_bit_cast(bf16x8, bs[swz_ch<CH>(fb_row[tn], ch)]);
+        fb[0][tn] = read_bt(bs, tn, 0);
     };
     auto slice_ready = [&](int kt) {  // slice kt landed; every wave is done with slice kt-1
       MOE_WAIT_LGKM0();  // fragment reads of slice kt-1 complete before its stages are refilled
@@ -462,14 +437,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 
   // Epilogue. Each lane owns slot row (lane & 31) of each 32-row band and,
   // per register quad q, output columns 8q + 4*(lane>>5) + 0..3 of a 32-wide
-  // column tile: 4 consecutive bf16 = one 8-byte piece.
-  //  gate/up, down: the pieces (silu(u) v for gate/up) go into a row-major
-  //           tile in the (now free) LDS ring with 16-byte chunks XOR-swizzled
-  //           by row, and the workgroup writes h or y out row by row, 16 bytes
-  //           per lane (fully coalesced; scattered 8-byte stores cost more).
-  //  gate/up keeping u and v (training), SwiGLU backward: the same through
-  //           the ring in two halves of BM/2 rows (a whole tile of their
-  //           outputs would not fit).
+  // column tile: 4 consecutive values = one 8-byte bf16 piece.
+  //  plain (da): the pieces go into a row-major tile in the (now free) LDS
+  //           ring with 16-byte chunks XOR-swizzled by row, and the workgroup
+  //           writes the rows out, 16 bytes per lane (fully coalesced;
+  //           scattered 8-byte stores cost more).
+  //  SwiGLU backward: the fp32 tile through the ring in two halves of BM/2
+  //           rows (a whole tile does not fit).
   if (SWB) {
     // SwiGLU backward: dh (the tile) with the saved u, v of the same columns
     // gives du = dh v silu'(u) and dv = dh silu(u), stored as [du | dv] rows.
@@ -554,78 +528,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
         }
       }
     }
-  } else if (SWIGLU && UV) {
-    // training: h and the kept u, v (row = [u | v], 2 N0 wide). The three
-    // bf16 tiles go through the freed ring in two halves of BM/2 rows (all
-    // three of a whole tile would not fit), 16-byte chunks XOR-swizzled by
-    // row, and are written out in whole rows, 16 bytes per lane.
-    constexpr int OC = Cfg::kOutCols;  // h (and u, v) columns per tile
-    constexpr int CPR = OC / 8;        // 16-byte chunks per output row
-    constexpr int HR = BM / 2;         // rows per half
-    constexpr int AB = HR * OC * 2;    // bytes of one staged half tile
-    static_assert(!SWIGLU || 3 * AB <= kRing * 16, "three half tiles fit the ring");
-    static_assert(WM == 2 && Cfg::TM == 4, "bands 2h, 2h+1 of each wave row are half h");
-    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "output row chunks: a power of two");
-    constexpr int RSTEP = Cfg::kThreads / CPR;
-    constexpr int NPASS = HR / RSTEP;
-    static_assert(Cfg::kThreads % CPR == 0 && HR % RSTEP == 0, "write-back passes");
-    constexpr int half = Cfg::TN / 2;
-    char* ot = reinterpret_cast<char*>(ring);
-    auto ot_addr = [&](int row, int col) {  // byte address of (row, col) in a half tile
-      return row * (OC * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col & 7) << 1);
-    };
-    const int rows_here = min(BM, seg1 - m0);
-    const int c = tid % CPR, r0 = tid / CPR;
-    const int col = c0 + c * 8;
-    MOE_WAIT_LGKM0();  // every wave's last fragment reads are done: the ring is free
-    wg_barrier();
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh) __syncthreads();  // the first half has been read out
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int tm = 2 * hh + b;
-        const int row = band_row(tm) - hh * HR + li;
-#pragma unroll
-        for (int tg = 0; tg < half; ++tg) {
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int lc = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * lk;
-            const f32x16& u = acc[tm][tg];
-            const f32x16& v = acc[tm][tg + half];
-            uint2 pk;
-            pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
-            pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
-            const int a = ot_addr(row, lc);
-            *reinterpret_cast<uint2*>(ot + a) = pk;
-            *reinterpret_cast<uint2*>(ot + AB + a) =
-                uint2{pack_bf16x2(u[4 * qd + 0], u[4 * qd + 1]), pack_bf16x2(u[4 * qd + 2], u[4 * qd + 3])};
-            *reinterpret_cast<uint2*>(ot + 2 * AB + a) =
-                uint2{pack_bf16x2(v[4 * qd + 0], v[4 * qd + 1]), pack_bf16x2(v[4 * qd + 2], v[4 * qd + 3])};
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int r = r0 + p * RSTEP;  // row in the half
-        const int a = ot_addr(r, c * 8);
-        const u32x4 hv = *reinterpret_cast<const u32x4*>(ot + a);
-        const u32x4 uv = *reinterpret_cast<const u32x4*>(ot + AB + a);
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(ot + 2 * AB + a);
-        const int tr = hh * HR + r;  // tile row
-        if (tr < rows_here && col < N0) {
-          *reinterpret_cast<u32x4*>(C + (size_t)(m0 + tr) * N0 + col) = hv;
-          uint16_t* uvrow = UV + (size_t)(m0 + tr) * (2 * N0);
-          *reinterpret_cast<u32x4*>(uvrow + col) = uv;
-          *reinterpret_cast<u32x4*>(uvrow + N0 + col) = vv;
-        }
-      }
-    }
   } else {
-    // The output tile (h = silu(u) v for gate/up, y for down) is staged
-    // row-major in the freed ring, 16-byte chunks XOR-swizzled by row, and
-    // written out in whole rows, 16 bytes per lane.
+    // The output tile (da) is staged row-major in the freed ring, 16-byte
+    // chunks XOR-swizzled by row, and written out in whole rows, 16 bytes per
+    // lane.
     constexpr int OC = Cfg::kOutCols;  // output columns per tile
     constexpr int CPR = OC / 8;        // 16-byte chunks per output row
     static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "output row chunks: a power of two");
@@ -635,40 +541,19 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
     auto ot_addr = [&](int row, int col) {  // byte address of (row, col) in the tile
       return row * (OC * 2) + (((col >> 3) ^ (row & (CPR - 1))) << 4) + ((col & 7) << 1);
     };
-    if (SWIGLU) {
-      constexpr int half = Cfg::TN / 2;
 #pragma unroll
-      for (int tm = 0; tm < Cfg::TM; ++tm) {
-        const int row = band_row(tm) + li;
+    for (int tm = 0; tm < Cfg::TM; ++tm) {
+      const int row = band_row(tm) + li;
 #pragma unroll
-        for (int tg = 0; tg < half; ++tg) {
+      for (int tn = 0; tn < Cfg::TN; ++tn) {
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int col = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * lk;
-            const f32x16& u = acc[tm][tg];
-            const f32x16& v = acc[tm][tg + half];
-            uint2 pk;
-            pk.x = pack_bf16x2(silu_mul(u[4 * qd + 0], v[4 * qd + 0]), silu_mul(u[4 * qd + 1], v[4 * qd + 1]));
-            pk.y = pack_bf16x2(silu_mul(u[4 * qd + 2], v[4 * qd + 2]), silu_mul(u[4 * qd + 3], v[4 * qd + 3]));
-            *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int tm = 0; tm < Cfg::TM; ++tm) {
-        const int row = band_row(tm) + li;
-#pragma unroll
-        for (int tn = 0; tn < Cfg::TN; ++tn) {
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int col = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
-            const f32x16& a = acc[tm][tn];
-            uint2 pk;
-            pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
-            pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
-            *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
-          }
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = wn * Cfg::kWaveCols + tn * 32 + 8 * qd + 4 * lk;
+          const f32x16& a = acc[tm][tn];
+          uint2 pk;
+          pk.x = pack_bf16x2(a[4 * qd + 0], a[4 * qd + 1]);
+          pk.y = pack_bf16x2(a[4 * qd + 2], a[4 * qd + 3]);
+          *reinterpret_cast<uint2*>(ot + ot_addr(row, col)) = pk;
         }
       }
     }
@@ -741,14 +626,16 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
 // touch 32 rows with 32 bytes each, and the CU's write path, not HBM, set
 // the pace).
 
-template <bool SWIGLU, bool WG = false>
+template <bool SWIGLU, bool WG = false, bool KEEP = false>
 __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm_row,
     const int32_t* __restrict__ expert_off, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, int K, int N0, uint16_t* __restrict__ C,
     uint32_t* __restrict__ queue, int M0 = 0, int msplit = 0, float* __restrict__ O0 = nullptr,
-    float* __restrict__ O1 = nullptr, const int32_t* __restrict__ kpad = nullptr) {
+    float* __restrict__ O1 = nullptr, const int32_t* __restrict__ kpad = nullptr,
+    uint16_t* __restrict__ UV = nullptr) {
   static_assert(!(WG && SWIGLU), "weight-gradient mode has a plain epilogue");
+  static_assert(!KEEP || SWIGLU, "u and v are kept by the gate/up launch");
   constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, NSA = 2, NSB = 3;
   using Cfg = TileCfg<BM, BN, WM, WN, SWIGLU>;
   constexpr int NW = WM * WN;
@@ -760,7 +647,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   constexpr int kStageA = BM * CH, kStageB = BN * CH;  // 16-byte units
   // output stores per thread and staging pass (a pass is 32 KiB x 2 of rows)
   constexpr int kStPass = 2 * 32768 / 16 / (WM * WN * kWave);
-  constexpr int kMaxPendSt = (SWIGLU ? 1 : 2) * kStPass;
+  constexpr int kMaxPendSt = (SWIGLU ? (KEEP ? 3 : 1) : 2) * kStPass;
   __shared__ u32x4 ring[NSA * kStageA + NSB * kStageB];
   auto stA = [&](int s) { return ring + (s % NSA) * kStageA; };
   auto stB = [&](int s) { return ring + NSA * kStageA + (s % NSB) * kStageB; };
@@ -1193,7 +1080,8 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
           return;
         }
         if (kt == 0 && NSB - 2 < KT) {
-          if (pend_st == 2 * kStPass) MOE_WAIT_VMCNT(kFirst + 2 * kStPass);
+          if (pend_st == 3 * kStPass) MOE_WAIT_VMCNT(kFirst + 3 * kStPass);
+          else if (pend_st == 2 * kStPass) MOE_WAIT_VMCNT(kFirst + 2 * kStPass);
           else if (pend_st == kStPass) MOE_WAIT_VMCNT(kFirst + kStPass);
           else MOE_WAIT_VMCNT(kFirst);
         } else if (kt > 0 && kt >= NSA - 1 && kt + NSB - 2 < KT) {
@@ -1370,7 +1258,8 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     // chunks XOR-swizzled by row; then whole rows are stored, 16 bytes per
     // lane. gate/up (h, 128 columns, 256 B a row): rows 0-127 and 128-255.
     // down (y, 256 columns, 512 B a row): two passes of 128 rows, 64 rows
-    // per region.
+    // per region. gate/up keeping u and v: three passes of the whole tile,
+    // h, then u, then v (the u | v rows of UV, 2 N0 wide).
     // byte offsets of the two regions in the ring (integers, so every access
     // below stays an LDS access the compiler can see)
     const int rgn0 = (gl % NSA) * kStageA * 16;
@@ -1379,8 +1268,8 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     constexpr int OC = Cfg::kOutCols;
     constexpr int CPR = OC / 8;                  // 16-byte chunks per row
     constexpr int RPR = 32768 / (OC * 2);         // rows per region
-    constexpr int PASSES = SWIGLU ? 1 : 2;
-    constexpr int PR = BM / PASSES;              // rows per pass
+    constexpr int PASSES = SWIGLU ? (KEEP ? 3 : 1) : 2;
+    constexpr int PR = SWIGLU ? BM : BM / PASSES;  // rows per pass
     static_assert(PR == 2 * RPR, "a pass fills both regions");
     auto ot_addr = [&](int row, int col) {  // row within the pass
       return ring_b + (row < RPR ? rgn0 : rgn1) + (row % RPR) * (OC * 2) +
@@ -1403,30 +1292,36 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     pend_st = 0;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
-      if (ps && rows_here <= ps * PR) break;  // uniform
-      if (ps) wg_barrier();  // the first pass has been read out
-      constexpr int TMP = Cfg::TM / PASSES;  // bands of this wave in one pass
+      if (!SWIGLU && ps && rows_here <= ps * PR) break;  // uniform
+      if (ps) wg_barrier();  // the previous pass has been read out
+      constexpr int TMP = SWIGLU ? Cfg::TM : Cfg::TM / PASSES;  // bands of this wave in one pass
 #pragma unroll
       for (int b = 0; b < TMP; ++b) {
-        const int tm = ps * TMP + b;
-        const int row = band_row(tm) - ps * PR + eli;
+        const int tm = SWIGLU ? b : ps * TMP + b;
+        const int row = band_row(tm) - (SWIGLU ? 0 : ps * PR) + eli;
         if (SWIGLU) {
           constexpr int half = Cfg::TN / 2;
 #pragma unroll
           for (int tg = 0; tg < half; ++tg) {
-            pro_part(b * half + tg);
+            if (ps == 0) pro_part(b * half + tg);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
               const int cc = wn * (Cfg::kWaveCols / 2) + tg * 32 + 8 * qd + 4 * elk;
               float u[4], v[4];
 #pragma unroll
               for (int e4 = 0; e4 < 4; ++e4) {
-                u[e4] = acc_read(acc[tm][tg][4 * qd + e4]);
-                v[e4] = acc_read(acc[tm][tg + half][4 * qd + e4]);
+                if (ps != 2) u[e4] = acc_read(acc[tm][tg][4 * qd + e4]);
+                if (ps != 1) v[e4] = acc_read(acc[tm][tg + half][4 * qd + e4]);
               }
               uint2 pk;
-              pk.x = pack_bf16x2(silu_mul(u[0], v[0]), silu_mul(u[1], v[1]));
-              pk.y = pack_bf16x2(silu_mul(u[2], v[2]), silu_mul(u[3], v[3]));
+              if (ps == 0) {  // h = silu(u) v
+                pk.x = pack_bf16x2(silu_mul(u[0], v[0]), silu_mul(u[1], v[1]));
+                pk.y = pack_bf16x2(silu_mul(u[2], v[2]), silu_mul(u[3], v[3]));
+              } else {  // u, then v
+                const float* w4 = ps == 1 ? u : v;
+                pk.x = pack_bf16x2(w4[0], w4[1]);
+                pk.y = pack_bf16x2(w4[2], w4[3]);
+              }
               *reinterpret_cast<uint2*>(ot_addr(row, cc)) = pk;
             }
             // one fragment pair at a time: the compiler would otherwise read
@@ -1454,8 +1349,12 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       }
       __syncthreads();
       const int n0e = opaque_s(N0);
-      const int last = rows_here - 1 - ps * PR;  // last row of the tile in this pass (>= 0)
-      uint16_t* gout = C + (size_t)(cm0 + ps * PR) * n0e + col;
+      const int last = rows_here - 1 - (SWIGLU ? 0 : ps * PR);  // last row of the tile in this pass
+      // h and y: rows of N0; u, v: the halves of UV's rows of 2 N0
+      const int ostride = (KEEP && ps > 0) ? 2 * n0e : n0e;
+      uint16_t* gout = (KEEP && ps > 0)
+                           ? UV + (size_t)cm0 * ostride + (ps == 2 ? n0e : 0) + col
+                           : C + (size_t)(cm0 + (SWIGLU ? 0 : ps * PR)) * n0e + col;
 #pragma unroll
       for (int p0 = 0; p0 < NPASS; p0 += 8) {
         u32x4 v[8];
@@ -1467,7 +1366,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
         }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          *reinterpret_cast<u32x4*>(gout + (size_t)rr[jj] * n0e) = v[jj];
+          *reinterpret_cast<u32x4*>(gout + (size_t)rr[jj] * ostride) = v[jj];
       }
       pend_st += NPASS;
       MOE_WAIT_LGKM0();
@@ -1630,8 +1529,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // from LDS per MFMA than 64 x 128 ones, which matters on a power-limited chip
 // (8 waves of 64 x 128 are ~1-3% slower here).
 constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 2, kWN = 2, kNSA = 2, kNSB = 3;
-// K slice and ring depths of the forward gate/up launch that keeps u, v
-constexpr int kFBK = 64, kFNSA = 2, kFNSB = 3;
 // Workspace of the persistent forward launches: the tile queue.
 constexpr size_t kExpertWorkspaceBytes = 256;
 static_assert(kQueueWords * 4 <= kExpertWorkspaceBytes, "queue fits the workspace");
@@ -1663,16 +1560,18 @@ int cu_count() {
 
 // Persistent forward launch over at most `tiles_ub` tiles: S workgroups per
 // XCD, S = CUs / 8 (one per CU), fewer when there are fewer tiles.
-template <bool SWIGLU>
+template <bool SWIGLU, bool KEEP = false>
 moe_status launch_persistent(const uint16_t* a, const int32_t* perm_row, const int32_t* expert_off,
                              int E, const uint16_t* b0, const uint16_t* b1, int K, int N0,
-                             uint16_t* c, uint32_t* queue, int64_t tiles_ub, hipStream_t stream) {
+                             uint16_t* c, uint32_t* queue, int64_t tiles_ub, hipStream_t stream,
+                             uint16_t* uv = nullptr) {
   const int cus = cu_count();
   if (cus <= 0) return MOE_ERR_DEVICE;
   const int64_t per_xcd = ceil_div(std::max<int64_t>(tiles_ub, 1), kXcd);
   const int S = (int)std::max<int64_t>(1, std::min<int64_t>(cus / kXcd, per_xcd));
-  hipLaunchKernelGGL(ffn_persistent_kernel<SWIGLU>, dim3(kXcd * S), dim3(256), 0, stream, a,
-                     perm_row, expert_off, E, b0, b1, K, N0, c, queue);
+  hipLaunchKernelGGL((ffn_persistent_kernel<SWIGLU, false, KEEP>), dim3(kXcd * S), dim3(256), 0,
+                     stream, a, perm_row, expert_off, E, b0, b1, K, N0, c, queue, 0, 0, nullptr,
+                     nullptr, nullptr, uv);
   return launch_status();
 }
 
@@ -1697,11 +1596,11 @@ void launch_dgrad_bf16(const uint16_t* a, int64_t rows, const int32_t* expert_of
                        const uint16_t* uv, uint16_t* c, hipStream_t stream) {
   const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(N0, kBN);
   if (uv)
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true, true>),
+    hipLaunchKernelGGL((dgrad_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, true>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, a, nullptr,
                        expert_off, E, w0, w1, K, N0, c, const_cast<uint16_t*>(uv), ksplit);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false, true, false>),
+    hipLaunchKernelGGL((dgrad_bf16_kernel<kBM, kBN, kBK, kWM, kWN, kNSA, kNSB, false>),
                        dim3(grid_for(tiles)), dim3(kWM * kWN * kWave), 0, stream, a, nullptr,
                        expert_off, E, w0, w1, K, N0, c, nullptr, ksplit);
 }
@@ -1761,24 +1660,26 @@ MOE_EXPORT moe_status moe_expert_gate_up_save(const void* x_disp, const int32_t*
                                               const int32_t* expert_off, int32_t T, int32_t E,
                                               int32_t k, int32_t d, int32_t F,
                                               const void* w_gate, const void* w_up, moe_dtype dt,
-                                              void* h, void* uv, hipStream_t stream) {
+                                              void* h, void* uv, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_ffn(T, E, k, d, F, dt);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x_disp || !perm_row || !expert_off || !w_gate || !w_up || !h || !uv) return MOE_ERR_ARG;
+  if (!workspace || workspace_bytes < kExpertWorkspaceBytes || (uintptr_t)workspace % 16)
+    return MOE_ERR_WORKSPACE;
   if (((uintptr_t)x_disp | (uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)h | (uintptr_t)uv) % 16)
     return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
   if (dt == MOE_BF16) {
     if (!dma_offsets_fit(rows, F, d)) return MOE_ERR_UNSUPPORTED;
-    constexpr int kOut = kBN / 2;
-    const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kOut);
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kFBK, kWM, kWN, kFNSA, kFNSB, true>),
-                       dim3(grid_for(tiles)),
-                       dim3(kWM * kWN * kWave), 0, stream, static_cast<const uint16_t*>(x_disp),
-                       perm_row, expert_off, E, static_cast<const uint16_t*>(w_gate),
-                       static_cast<const uint16_t*>(w_up), d, F, static_cast<uint16_t*>(h),
-                       static_cast<uint16_t*>(uv));
+    const int64_t tiles = mtile_upper(rows, E, kBM) * ceil_div(F, kBN / 2);
+    return launch_persistent<true, true>(static_cast<const uint16_t*>(x_disp), perm_row,
+                                         expert_off, E, static_cast<const uint16_t*>(w_gate),
+                                         static_cast<const uint16_t*>(w_up), d, F,
+                                         static_cast<uint16_t*>(h),
+                                         static_cast<uint32_t*>(workspace), tiles, stream,
+                                         static_cast<uint16_t*>(uv));
   } else {
     const int64_t tiles = mtile_upper(rows, E, 64) * ceil_div(F, 64);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(tiles)), dim3(256), 0, stream,

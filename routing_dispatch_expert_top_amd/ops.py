@@ -57,7 +57,7 @@ def lib():
             "moe_combine": (C.c_int, [p, p, p, i32, i32, i32, C.c_int, p, p]),
             "moe_plan_placement": (C.c_int, [p, p, i32, i32, i32, i32, p]),
             "moe_expert_gate_up_save": (C.c_int, [p, p, p, i32, i32, i32, i32, i32, p, p,
-                                                  C.c_int, p, p, p]),
+                                                  C.c_int, p, p, p, sz, p]),
             "moe_combine_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, C.c_int, p, p, p]),
             "moe_expert_bwd_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
             "moe_expert_down_bwd": (C.c_int, [p, p, p, p, i32, i32, i32, i32, i32, p, C.c_int,
@@ -295,14 +295,15 @@ def moe_grouped_ffn(x_disp, perm_row, expert_off, T, k, w_gate, w_up, w_down, h=
 # ---------------------------------------------------------------- backward
 
 def moe_expert_gate_up_save(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=None, uv=None,
-                            stream=None):
+                            workspace=None, stream=None):
     E, F, d = w_gate.shape
     dev, dt = x_disp.device, x_disp.dtype
     h = torch.empty((T * k, F), dtype=dt, device=dev) if h is None else h
     uv = torch.empty((T * k, 2 * F), dtype=dt, device=dev) if uv is None else uv
+    ws = expert_workspace(dev) if workspace is None else workspace
     _check("moe_expert_gate_up_save", lib().moe_expert_gate_up_save(
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
-        dtype_code(x_disp), _ptr(h), _ptr(uv), _stream(stream)))
+        dtype_code(x_disp), _ptr(h), _ptr(uv), _ptr(ws), ws.numel(), _stream(stream)))
     return h, uv
 
 

@@ -21,7 +21,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert ops.status_str(0) == "ok"
     assert "workspace" in ops.status_str(3)
     assert ops.status_str(99) == "unknown status"
