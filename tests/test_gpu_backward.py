@@ -231,6 +231,45 @@ def test_expert_bwd_workspace_reused():
     per_expert_close("dw_up", outs[0][4], rdwu, eo)
 
 
+SAVE_CASES = [
+    synth.custom(name="bf16_save_ragged", T=700, d=256, E=6, k=2, F=320, G=2, dtype="bf16",
+                 clusters=2),
+    synth.custom(name="bf16_save_long_k", T=1500, d=1024, E=4, k=2, F=192, G=2, dtype="bf16",
+                 clusters=2),
+]
+
+
+@pytest.mark.parametrize("w", SAVE_CASES, ids=[w.name for w in SAVE_CASES])
+def test_gate_up_save_outputs(w):
+    """The training gate/up (persistent launch, h then u then v staged and
+    stored in turn) against the plain forward gate/up (h bit for bit) and
+    against the fp64 reference's u, v and h in slot order. F = 320 leaves a
+    half-filled column tile; d = 1024 runs 16 K slices; experts of 214 to
+    764 slots leave ragged m-tiles."""
+    print(f"case gate_up_save {w.name} {w.tag()}", flush=True)
+    inp = synth.make(w)
+    lay = ops.Layer(w.T, w.d, w.E, w.k, w.F, w.G, torch.bfloat16, "cuda", w.n_groups,
+                    w.topk_groups)
+    lay.route(dev(inp["logits"]))
+    lay.dispatch(dev(inp["x"]), dev(inp["place"]))
+    L = lay.lay
+    wg, wu = dev(inp["w_gate"]), dev(inp["w_up"])
+    h_plain = ops.moe_expert_gate_up(L["x_disp"], L["perm_row"], L["expert_off"], w.T, w.k, wg, wu)
+    h, uv = ops.moe_expert_gate_up_save(L["x_disp"], L["perm_row"], L["expert_off"], w.T, w.k,
+                                        wg, wu)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_plain)
+    idx, gates = oracle.route(inp["logits"], w.k)
+    assert np.array_equal(host(lay.topk_idx), idx)
+    ref = OB.layer_backward(idx, gates, synth.to_f64(inp["x"], "bf16"),
+                            synth.to_f64(inp["w_gate"], "bf16"), synth.to_f64(inp["w_up"], "bf16"),
+                            synth.to_f64(inp["w_down"], "bf16"), np.zeros((w.T, w.d)))
+    g_uv = host(uv)
+    assert_close("u", g_uv[:, :w.F], ref["u"], TAU["bf16"])
+    assert_close("v", g_uv[:, w.F:], ref["v"], TAU["bf16"])
+    assert_close("h", host(h), ref["h"], TAU["bf16"])
+
+
 def _gpu_train_step(w, inp, dout, place):
     """Forward (saving u, v) and every backward step on the GPU."""
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
