@@ -1164,7 +1164,9 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       // fp32 gradient rows through the two ring stages the prologue left
       // free (32 rows each), four passes of 64 tile rows: each wave writes
       // its band's 16-byte pieces (chunk index XOR-ed with the row), then
-      // every wave stores whole 1 KiB rows, one per instruction.
+      // every wave stores whole 1 KiB rows, one per instruction, as
+      // non-temporal stores: nothing reads the gradients back, and whole
+      // lines need no merging in the L2.
       pend_st = 0;
       if (cur.e >= 0) {
         const int etid = opaque_tid();
@@ -1206,7 +1208,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
               const int row = cm0 + 64 * ps + wave + 4 * (i0 + i);
               float* orow = row < msplit ? O0 + ((size_t)cur.e * msplit + row) * n0e
                                          : O1 + ((size_t)cur.e * (M0 - msplit) + (row - msplit)) * n0e;
-              if (colok) *reinterpret_cast<u32x4*>(orow + c0 + 4 * ln) = v[i];
+              if (colok) __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(orow + c0 + 4 * ln));
             }
           }
           pend_st += 16;
