@@ -712,7 +712,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const uint64_t bal = __ballot(incl * NT > n);
     const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)bal) - 1);
     int first = __builtin_amdgcn_readlane(excl, L);
-    Tile t{0, 0, 0, 0, 0, 0, 0};
+    Tile t{0, 0, 0, 0, 0};
     int lo = expert_off[min(4 * L, E)];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
