@@ -16,12 +16,17 @@
 // and B into a ring of LDS stages with direct-to-LDS loads (16-byte chunks,
 // XOR-swizzled so the MFMA fragment reads are free of bank conflicts) while
 // the MFMAs consume an earlier slice.
-// The tile list is derived on the device from expert_off (each workgroup
-// scans it in LDS), so no host round trip is needed; blocks are remapped so
-// that consecutive tiles of one (expert, N-tile) land on the same XCD and
-// share its L2 copy of the weight tile.
+// The tile list is derived on the device from expert_off, so no host round
+// trip is needed. The forward launches are persistent: one workgroup per CU
+// walks its XCD's share of the tile list in order, claiming tiles from a
+// per-XCD counter in the caller's workspace, so that the tiles running at
+// once on an XCD are neighbours that share weight panels and activation
+// tiles in its L2. The same kernel, in a weight-gradient mode, computes the
+// backward's weight gradients; a one-tile-per-workgroup kernel computes its
+// data gradients.
 //
-// fp32 path: a plain LDS-tiled FMA kernel with the same schedule.
+// fp32 path: the fp32 matrix cores (v_mfma_f32_32x32x2_f32), 64 x 64 tiles
+// staged K-major in LDS.
 #include "moe_internal.h"
 #include "gemm_common.h"
 
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     const uint64_t bal = __ballot(incl * NT > n);
     const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)bal) - 1);
     int first = __builtin_amdgcn_readlane(excl, L);
-    Tile t{0, 0, 0, 0, 0};
+    Tile t{0, 0, 0, 0, 0, 0, 0};
     int lo = expert_off[min(4 * L, E)];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
