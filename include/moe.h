@@ -66,7 +66,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Version of this ABI (MOE_ABI_VERSION of the build). */
 int moe_abi_version(void);
 
-/* Static string naming a status code. */
+/* Static string naming a status code. It takes an int, not a moe_status, so
+   that any value (a code from a newer build, a corrupted one) gets a string:
+   "unknown status" outside the enumeration. */
 const char* moe_status_str(int status);
 
 /*
