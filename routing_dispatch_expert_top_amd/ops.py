@@ -78,8 +78,23 @@ def lib():
         for name, (res, args) in sig.items():
             f = getattr(L, name)
             f.restype, f.argtypes = res, args
+        # The signatures above are those of include/moe.h: a library built
+        # from another version of it would be called with the wrong arguments.
+        want, got = header_abi_version(), L.moe_abi_version()
+        if got != want:
+            raise RuntimeError(f"{LIB_PATH} implements ABI {got} but include/moe.h declares "
+                               f"ABI {want}: rebuild it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
         _lib = L
     return _lib
+
+
+def header_abi_version() -> int:
+    """MOE_ABI_VERSION as include/moe.h defines it."""
+    m = re.search(r"#define\s+MOE_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    if m is None:
+        raise RuntimeError(f"{HEADER} defines no MOE_ABI_VERSION")
+    return int(m.group(1))
 
 
 def header_functions():

@@ -27,6 +27,16 @@ def test_version_and_status_strings(L):
     assert ops.status_str(99) == "unknown status"
 
 
+def test_library_abi_must_match_the_header(L, monkeypatch):
+    # the binding's signatures are the header's: a library of another ABI
+    # version is refused when it is loaded
+    assert ops.header_abi_version() == L.moe_abi_version()
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "header_abi_version", lambda: L.moe_abi_version() + 1)
+    with pytest.raises(RuntimeError, match="rebuild"):
+        ops.lib()
+
+
 def test_workspace_bytes_host_only(L):
     a = ops.moe_dispatch_workspace_bytes(8192, 128, 8, 16)
     b = ops.moe_dispatch_workspace_bytes(16384, 128, 8, 16)
