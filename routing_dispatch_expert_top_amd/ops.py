@@ -133,6 +133,33 @@ def _stream(stream):
     return stream
 
 
+_I32, _F32 = torch.int32, torch.float32
+
+
+def _need(fn, name, t, numel, dtype=None):
+    """Refuse a tensor the call would read or write past its end (the C ABI
+    takes raw pointers and cannot check), or one of the wrong element type."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{fn}: {name} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{fn}: {name} holds {t.numel()} elements, the call uses {numel}")
+
+
+def _rows(fn, name, t, width, dtype=None):
+    """A buffer of slot rows: how many the call touches (expert_off[E], at
+    most T*k) is known only on the device, so only the row width and the
+    element type are checked."""
+    if t is None:
+        return
+    _need(fn, name, t, 0, dtype)
+    if t.numel() % width:
+        raise ValueError(f"{fn}: {name} must hold whole rows of {width} elements")
+
+
 def dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return MOE_F32
@@ -150,6 +177,8 @@ def moe_route(logits, k, n_groups=1, topk_groups=1, topk_idx=None, gates=None, s
     gates = torch.empty((T, k), dtype=torch.float32, device=dev) if gates is None else gates
     if logits.dtype != torch.float32:
         raise TypeError("logits must be float32")
+    _need("moe_route", "topk_idx", topk_idx, T * k, _I32)
+    _need("moe_route", "gates", gates, T * k, _F32)
     _check("moe_route", lib().moe_route(_ptr(logits), T, E, k, n_groups, topk_groups,
                                         _ptr(topk_idx), _ptr(gates), _stream(stream)))
     return topk_idx, gates
@@ -158,6 +187,8 @@ def moe_route(logits, k, n_groups=1, topk_groups=1, topk_idx=None, gates=None, s
 def moe_coact_hist(topk_idx, E, coact=None, stream=None):
     T, k = topk_idx.shape
     coact = torch.zeros((E, E), dtype=torch.int32, device=topk_idx.device) if coact is None else coact
+    _need("moe_coact_hist", "topk_idx", topk_idx, T * k, _I32)
+    _need("moe_coact_hist", "coact", coact, E * E, _I32)
     _check("moe_coact_hist", lib().moe_coact_hist(_ptr(topk_idx), T, E, k, _ptr(coact),
                                                   _stream(stream)))
     return coact
@@ -183,6 +214,21 @@ def alloc_layout(T, E, k, G, device, d=None, dtype=None):
     return out
 
 
+def _need_layout(fn, topk_idx, E, place, G, x, out):
+    T, k = topk_idx.shape
+    _need(fn, "topk_idx", topk_idx, T * k, _I32)
+    _need(fn, "place", place, E, _I32)
+    for name, n in (("rank_mask", T), ("rank_off", G + 1), ("disp_token", T * k),
+                    ("expert_off", E + 1), ("perm_row", T * k), ("slot_of", T * k)):
+        _need(fn, name, out[name], n, _I32)
+    if x is not None:
+        if x.dim() != 2 or x.shape[0] != T:
+            raise ValueError(f"{fn}: x must be [T, d] with T = {T}")
+        _need(fn, "x_disp", out.get("x_disp"), T * k * x.shape[1], x.dtype)
+        if out.get("x_disp") is None:
+            raise ValueError(f"{fn}: x given without an x_disp buffer")
+
+
 def moe_dispatch_layout(topk_idx, E, place, G, x=None, out=None, stream=None):
     """Returns the dict of outputs (rank_mask holds uint32 bits in an int32 tensor)."""
     T, k = topk_idx.shape
@@ -190,6 +236,7 @@ def moe_dispatch_layout(topk_idx, E, place, G, x=None, out=None, stream=None):
     if out is None:
         out = alloc_layout(T, E, k, G, topk_idx.device, d, x.dtype if x is not None else None)
     dt = dtype_code(x) if x is not None else MOE_F32
+    _need_layout("moe_dispatch_layout", topk_idx, E, place, G, x, out)
     ws = out["workspace"]
     _check("moe_dispatch_layout", lib().moe_dispatch_layout(
         _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(x), d or 0, dt,
@@ -208,6 +255,7 @@ def moe_dispatch_layout_noalloc(topk_idx, E, place, G, x=None, out=None, stream=
     if out is None:
         out = alloc_layout(T, E, k, G, topk_idx.device, d, x.dtype if x is not None else None)
     dt = dtype_code(x) if x is not None else MOE_F32
+    _need_layout("moe_dispatch_layout_noalloc", topk_idx, E, place, G, x, out)
     _check("moe_dispatch_layout_noalloc", lib().moe_dispatch_layout_noalloc(
         _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(x), d or 0, dt,
         _ptr(out["rank_mask"]), _ptr(out["rank_off"]), _ptr(out["disp_token"]),
@@ -230,6 +278,10 @@ def moe_replica_layout(topk_idx, E, rep_mask, G, ranks_per_node, x=None, out=Non
         out["rank_of"] = torch.empty(T * k, dtype=torch.int32, device=dev)
         out["node_mask"] = torch.empty(T, dtype=torch.int32, device=dev)
     dt = dtype_code(x) if x is not None else MOE_F32
+    _need_layout("moe_replica_layout", topk_idx, E, None, G, x, out)
+    _need("moe_replica_layout", "rep_mask", rep_mask, E, _I32)
+    _need("moe_replica_layout", "rank_of", out["rank_of"], T * k, _I32)
+    _need("moe_replica_layout", "node_mask", out["node_mask"], T, _I32)
     ws = out["workspace"]
     _check("moe_replica_layout", lib().moe_replica_layout(
         _ptr(topk_idx), T, E, k, _ptr(rep_mask), G, ranks_per_node, _ptr(x), d or 0, dt,
@@ -256,6 +308,18 @@ def moe_token_shuffle(want_idx, aff, x=None, out=None, stream=None):
         if x is not None:
             out["x_shuf"] = torch.empty_like(x)
     dt = dtype_code(x) if x is not None else MOE_F32
+    fn = "moe_token_shuffle"
+    _need(fn, "want_idx", want_idx, T * k, _I32)
+    _need(fn, "aff", aff, E * G, _I32)
+    for name in ("dest", "perm", "pos"):
+        _need(fn, name, out[name], T, _I32)
+    _need(fn, "rank_off", out["rank_off"], G + 1, _I32)
+    if x is not None:
+        if x.dim() != 2 or x.shape[0] != T:
+            raise ValueError(f"{fn}: x must be [T, d] with T = {T}")
+        if out.get("x_shuf") is None:
+            raise ValueError(f"{fn}: x given without an x_shuf buffer")
+        _need(fn, "x_shuf", out["x_shuf"], x.numel(), x.dtype)
     ws = out["workspace"]
     _check("moe_token_shuffle", lib().moe_token_shuffle(
         _ptr(want_idx), T, E, k, _ptr(aff), G, _ptr(x), x.shape[1] if x is not None else 0, dt,
@@ -272,11 +336,33 @@ def expert_workspace(device):
                        device=device)
 
 
+def _need_gate_up(fn, x_disp, perm_row, expert_off, T, k, w_gate, w_up):
+    E, F, d = w_gate.shape
+    dt = x_disp.dtype
+    if tuple(w_up.shape) != (E, F, d):
+        raise ValueError(f"{fn}: w_up must be [E, F, d] like w_gate")
+    if x_disp.dim() != 2 or x_disp.shape[1] != d:
+        raise ValueError(f"{fn}: x_disp must be [rows, d] with d = {d}")
+    _need(fn, "w_gate", w_gate, 0, dt)
+    _need(fn, "w_up", w_up, 0, dt)
+    _need(fn, "perm_row", perm_row, T * k, _I32)
+    _need(fn, "expert_off", expert_off, E + 1, _I32)
+
+
+def _need_down(fn, h, expert_off, T, k, w_down):
+    E, d, F = w_down.shape
+    _rows(fn, "h", h, F)
+    _need(fn, "w_down", w_down, 0, h.dtype)
+    _need(fn, "expert_off", expert_off, E + 1, _I32)
+
+
 def moe_expert_gate_up(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=None, workspace=None,
                        stream=None):
     E, F, d = w_gate.shape
     h = torch.empty((T * k, F), dtype=x_disp.dtype, device=x_disp.device) if h is None else h
     ws = expert_workspace(x_disp.device) if workspace is None else workspace
+    _need_gate_up("moe_expert_gate_up", x_disp, perm_row, expert_off, T, k, w_gate, w_up)
+    _rows("moe_expert_gate_up", "h", h, F, x_disp.dtype)
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
         dtype_code(x_disp), _ptr(h), _ptr(ws), ws.numel(), _stream(stream)))
@@ -287,6 +373,8 @@ def moe_expert_down(h, expert_off, T, k, w_down, y=None, workspace=None, stream=
     E, d, F = w_down.shape
     y = torch.empty((T * k, d), dtype=h.dtype, device=h.device) if y is None else y
     ws = expert_workspace(h.device) if workspace is None else workspace
+    _need_down("moe_expert_down", h, expert_off, T, k, w_down)
+    _rows("moe_expert_down", "y", y, d, h.dtype)
     _check("moe_expert_down", lib().moe_expert_down(
         _ptr(h), _ptr(expert_off), T, E, k, d, F, _ptr(w_down), dtype_code(h), _ptr(y), _ptr(ws),
         ws.numel(), _stream(stream)))
@@ -300,6 +388,12 @@ def moe_grouped_ffn(x_disp, perm_row, expert_off, T, k, w_gate, w_up, w_down, h=
     h = torch.empty((T * k, F), dtype=dt, device=dev) if h is None else h
     y = torch.empty((T * k, d), dtype=dt, device=dev) if y is None else y
     ws = expert_workspace(dev) if workspace is None else workspace
+    _need_gate_up("moe_grouped_ffn", x_disp, perm_row, expert_off, T, k, w_gate, w_up)
+    if tuple(w_down.shape) != (E, d, F):
+        raise ValueError("moe_grouped_ffn: w_down must be [E, d, F]")
+    _need("moe_grouped_ffn", "w_down", w_down, 0, dt)
+    _rows("moe_grouped_ffn", "h", h, F, dt)
+    _rows("moe_grouped_ffn", "y", y, d, dt)
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), dtype_code(x_disp), _ptr(h), _ptr(y), _ptr(ws), ws.numel(),
@@ -316,6 +410,9 @@ def moe_expert_gate_up_save(x_disp, perm_row, expert_off, T, k, w_gate, w_up, h=
     h = torch.empty((T * k, F), dtype=dt, device=dev) if h is None else h
     uv = torch.empty((T * k, 2 * F), dtype=dt, device=dev) if uv is None else uv
     ws = expert_workspace(dev) if workspace is None else workspace
+    _need_gate_up("moe_expert_gate_up_save", x_disp, perm_row, expert_off, T, k, w_gate, w_up)
+    _rows("moe_expert_gate_up_save", "h", h, F, dt)
+    _rows("moe_expert_gate_up_save", "uv", uv, 2 * F, dt)
     _check("moe_expert_gate_up_save", lib().moe_expert_gate_up_save(
         _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate), _ptr(w_up),
         dtype_code(x_disp), _ptr(h), _ptr(uv), _ptr(ws), ws.numel(), _stream(stream)))
@@ -327,6 +424,14 @@ def moe_combine_bwd(dout, y, slot_of, gates, T, k, dy=None, dgates=None, stream=
     dy = torch.empty((T * k, d), dtype=dout.dtype, device=dout.device) if dy is None else dy
     dgates = (torch.empty((T, k), dtype=torch.float32, device=dout.device)
               if dgates is None else dgates)
+    fn = "moe_combine_bwd"
+    if dout.dim() != 2 or dout.shape[0] != T:
+        raise ValueError(f"{fn}: dout must be [T, d] with T = {T}")
+    _rows(fn, "y", y, d, dout.dtype)
+    _need(fn, "slot_of", slot_of, T * k, _I32)
+    _need(fn, "gates", gates, T * k, _F32)
+    _rows(fn, "dy", dy, d, dout.dtype)
+    _need(fn, "dgates", dgates, T * k, _F32)
     _check("moe_combine_bwd", lib().moe_combine_bwd(
         _ptr(dout), _ptr(y), _ptr(slot_of), _ptr(gates), T, k, d, dtype_code(dout), _ptr(dy),
         _ptr(dgates), _stream(stream)))
@@ -350,6 +455,12 @@ def moe_expert_down_bwd(dy, h, uv, expert_off, T, k, w_down, duv=None, dw_down=N
     dw_down = (torch.empty((E, d, F), dtype=torch.float32, device=dev)
                if dw_down is None else dw_down)
     ws = bwd_workspace(T, E, k, d, F, dev) if workspace is None else workspace
+    fn = "moe_expert_down_bwd"
+    _need_down(fn, h, expert_off, T, k, w_down)
+    _rows(fn, "dy", dy, d, h.dtype)
+    _rows(fn, "uv", uv, 2 * F, h.dtype)
+    _rows(fn, "duv", duv, 2 * F, h.dtype)
+    _need(fn, "dw_down", dw_down, E * d * F, _F32)
     _check("moe_expert_down_bwd", lib().moe_expert_down_bwd(
         _ptr(dy), _ptr(h), _ptr(uv), _ptr(expert_off), T, E, k, d, F, _ptr(w_down),
         dtype_code(dy), _ptr(duv), _ptr(dw_down), _ptr(ws), ws.numel(), _stream(stream)))
@@ -365,6 +476,12 @@ def moe_expert_gate_up_bwd(duv, x_disp, perm_row, expert_off, T, k, w_gate, w_up
     dw_gate = torch.empty((E, F, d), **f32) if dw_gate is None else dw_gate
     dw_up = torch.empty((E, F, d), **f32) if dw_up is None else dw_up
     ws = bwd_workspace(T, E, k, d, F, dev) if workspace is None else workspace
+    fn = "moe_expert_gate_up_bwd"
+    _need_gate_up(fn, x_disp, perm_row, expert_off, T, k, w_gate, w_up)
+    _rows(fn, "duv", duv, 2 * F, x_disp.dtype)
+    _rows(fn, "da", da, d, x_disp.dtype)
+    _need(fn, "dw_gate", dw_gate, E * F * d, _F32)
+    _need(fn, "dw_up", dw_up, E * F * d, _F32)
     _check("moe_expert_gate_up_bwd", lib().moe_expert_gate_up_bwd(
         _ptr(duv), _ptr(x_disp), _ptr(perm_row), _ptr(expert_off), T, E, k, d, F, _ptr(w_gate),
         _ptr(w_up), dtype_code(duv), _ptr(da), _ptr(dw_gate), _ptr(dw_up), _ptr(ws), ws.numel(),
@@ -375,6 +492,9 @@ def moe_expert_gate_up_bwd(duv, x_disp, perm_row, expert_off, T, k, w_gate, w_up
 def moe_dispatch_bwd(da, slot_of, T, k, dx=None, stream=None):
     d = da.shape[1]
     dx = torch.empty((T, d), dtype=da.dtype, device=da.device) if dx is None else dx
+    _rows("moe_dispatch_bwd", "da", da, d)
+    _need("moe_dispatch_bwd", "slot_of", slot_of, T * k, _I32)
+    _need("moe_dispatch_bwd", "dx", dx, T * d, da.dtype)
     _check("moe_dispatch_bwd", lib().moe_dispatch_bwd(
         _ptr(da), _ptr(slot_of), T, k, d, dtype_code(da), _ptr(dx), _stream(stream)))
     return dx
@@ -384,6 +504,10 @@ def moe_route_bwd(gates, dgates, topk_idx, E, dlogits=None, stream=None):
     T, k = gates.shape
     dlogits = (torch.empty((T, E), dtype=torch.float32, device=gates.device)
                if dlogits is None else dlogits)
+    _need("moe_route_bwd", "gates", gates, T * k, _F32)
+    _need("moe_route_bwd", "dgates", dgates, T * k, _F32)
+    _need("moe_route_bwd", "topk_idx", topk_idx, T * k, _I32)
+    _need("moe_route_bwd", "dlogits", dlogits, T * E, _F32)
     _check("moe_route_bwd", lib().moe_route_bwd(
         _ptr(gates), _ptr(dgates), _ptr(topk_idx), T, E, k, _ptr(dlogits), _stream(stream)))
     return dlogits
@@ -402,6 +526,9 @@ def moe_validate_routing(logits, topk_idx, E, place=None, G=1, stream=None):
     T, k = topk_idx.shape if topk_idx is not None else (logits.shape[0], 1)
     ref = next(a for a in (logits, topk_idx, place) if a is not None)
     err = torch.zeros(1, dtype=torch.int32, device=ref.device)
+    _need("moe_validate_routing", "logits", logits, T * E, _F32)
+    _need("moe_validate_routing", "topk_idx", topk_idx, T * k, _I32)
+    _need("moe_validate_routing", "place", place, E, _I32)
     _check("moe_validate_routing", lib().moe_validate_routing(
         _ptr(logits), _ptr(topk_idx), T, E, k, _ptr(place), G, _ptr(err), _stream(stream)))
     torch.cuda.synchronize(ref.device)  # the kernel may run on another stream than torch's
@@ -440,6 +567,10 @@ def moe_plan_placement(coact, load, G, ranks_per_node=1, swap_passes=8):
 def moe_combine(y, slot_of, gates, T, k, out=None, stream=None):
     d = y.shape[1]
     out = torch.empty((T, d), dtype=y.dtype, device=y.device) if out is None else out
+    _rows("moe_combine", "y", y, d)
+    _need("moe_combine", "slot_of", slot_of, T * k, _I32)
+    _need("moe_combine", "gates", gates, T * k, _F32)
+    _need("moe_combine", "out", out, T * d, y.dtype)
     _check("moe_combine", lib().moe_combine(_ptr(y), _ptr(slot_of), _ptr(gates), T, k, d,
                                             dtype_code(y), _ptr(out), _stream(stream)))
     return out

@@ -4,6 +4,7 @@ these calls touches a device, so they run without a GPU)."""
 import ctypes as C
 
 import pytest
+import torch
 
 from routing_dispatch_expert_top_amd import ops
 
@@ -151,3 +152,46 @@ def test_backward_expert_calls_need_their_workspace():
     st = L.moe_expert_down_bwd(fake, fake, fake, fake, T, E, k, 96, F, fake, ops.MOE_BF16, fake,
                                fake, fake, need, None)
     assert st == ops.MOE_ERR_UNSUPPORTED  # d not a multiple of 64
+
+
+def test_binding_refuses_undersized_or_mistyped_buffers(L):
+    # The C ABI takes raw pointers; the binding checks every buffer's size and
+    # element type before the call (host tensors here: the checks come first).
+    T, k, E, d, F = 8, 2, 4, 64, 64
+    i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+    slot_of = torch.zeros(T * k, dtype=i32)
+    gates = torch.zeros(T * k, dtype=f32)
+    y = torch.zeros(T * k, d, dtype=bf)
+    with pytest.raises(ValueError, match="out holds"):
+        ops.moe_combine(y, slot_of, gates, T, k, out=torch.zeros(T - 1, d, dtype=bf))
+    with pytest.raises(TypeError, match="slot_of must be"):
+        ops.moe_combine(y, slot_of.long(), gates, T, k, out=torch.zeros(T, d, dtype=bf))
+    logits = torch.zeros(T, E, dtype=f32)
+    with pytest.raises(ValueError, match="gates holds"):
+        ops.moe_route(logits, k, gates=torch.zeros(T * k - 1, dtype=f32))
+    x_disp = torch.zeros(T * k, d, dtype=bf)
+    wg = torch.zeros(E, F, d, dtype=bf)
+    with pytest.raises(ValueError, match="w_up must be"):
+        ops.moe_expert_gate_up(x_disp, slot_of, torch.zeros(E + 1, dtype=i32), T, k, wg,
+                               torch.zeros(E, F + 64, d, dtype=bf), workspace=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="w_gate must be"):
+        ops.moe_expert_gate_up(x_disp, slot_of, torch.zeros(E + 1, dtype=i32), T, k, wg.float(),
+                               wg.float(), workspace=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="expert_off holds"):
+        ops.moe_expert_down(torch.zeros(T * k, F, dtype=bf), torch.zeros(E, dtype=i32), T, k,
+                            torch.zeros(E, d, F, dtype=bf), workspace=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="whole rows"):  # slot rows: width and type only
+        ops.moe_expert_down(torch.zeros(T * k, F, dtype=bf), torch.zeros(E + 1, dtype=i32), T, k,
+                            torch.zeros(E, d, F, dtype=bf), y=torch.zeros(T * k * d + 3, dtype=bf),
+                            workspace=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="dw_down holds"):
+        ops.moe_expert_down_bwd(y, torch.zeros(T * k, F, dtype=bf), torch.zeros(T * k, 2 * F, dtype=bf),
+                                torch.zeros(E + 1, dtype=i32), T, k, torch.zeros(E, d, F, dtype=bf),
+                                dw_down=torch.zeros(E * d * F - 1, dtype=f32),
+                                workspace=torch.zeros(1, dtype=torch.uint8))
+    topk = torch.zeros(T, k, dtype=i32)
+    out = ops.alloc_layout(T, E, k, 2, "cpu", d, bf)
+    out["perm_row"] = out["perm_row"][:-1]
+    with pytest.raises(ValueError, match="perm_row holds"):
+        ops.moe_dispatch_layout(topk, E, torch.zeros(E, dtype=i32), 2,
+                                x=torch.zeros(T, d, dtype=bf), out=out)
