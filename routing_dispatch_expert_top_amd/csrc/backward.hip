@@ -43,7 +43,11 @@ namespace {
 // KK > 0: k == KK at compile time (the common values), so the token's slots
 // and gates are read once into registers and every choice's y chunk is
 // loaded before any is used; KK == 0: runtime k <= kMaxK.
-template <bool BF16, int KK>
+// HOLD: the row is at most kBwdHoldBlocks 1 KiB blocks; dout's row is held
+// in registers, every y block is read first, and the dy rows are written
+// afterwards, each as one contiguous run.
+constexpr int kBwdHoldBlocks = 8;
+template <bool BF16, int KK, bool HOLD>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const u32x4* __restrict__ dout, const u32x4* __restrict__ y,
     const int32_t* __restrict__ slot_of, const float* __restrict__ gates, int T, int k_rt,
@@ -74,9 +78,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   // step, all of their loads issued before any is used.
   const int nblk = (row_vecs + kWave - 1) / kWave;
   const int sb = t % nblk;
-  auto block = [&](auto chk_c, int c, const u32x4& ov, const u32x4 (&yv)[KM]) {
-    constexpr bool CHK = decltype(chk_c)::value;
-    float of[8];
+  auto widen = [&](const u32x4& ov, float (&of)[8]) {
     if (BF16) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -87,50 +89,120 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) of[q] = __uint_as_float(ov[q]);
     }
+  };
+  // the dot products' share of one block (fp32, in element order)
+  auto dots = [&](auto chk_c, const u32x4& ov, const u32x4 (&yv)[KM]) {
+    constexpr bool CHK = decltype(chk_c)::value;
+    float of[8];
+    widen(ov, of);
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j >= k || (CHK && !live[j])) continue;
-      const float g = gt[j];
-      u32x4 w;
       if (BF16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           dot[j] = fmaf(of[2 * q], bf16lo(yv[j][q]), dot[j]);
           dot[j] = fmaf(of[2 * q + 1], bf16hi(yv[j][q]), dot[j]);
-          w[q] = pack_bf16x2(g * of[2 * q], g * of[2 * q + 1]);
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          dot[j] = fmaf(of[q], __uint_as_float(yv[j][q]), dot[j]);
-          w[q] = __float_as_uint(g * of[q]);
-        }
+        for (int q = 0; q < 4; ++q) dot[j] = fmaf(of[q], __uint_as_float(yv[j][q]), dot[j]);
       }
-      dy[(size_t)sl[j] * row_vecs + c] = w;
     }
+  };
+  // g times one dout block, in the activation type
+  auto scaled = [&](const u32x4& ov, float g) {
+    float of[8];
+    widen(ov, of);
+    u32x4 w;
+    if (BF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(g * of[2 * q], g * of[2 * q + 1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = __float_as_uint(g * of[q]);
+    }
+    return w;
+  };
+  auto block = [&](auto chk_c, int c, const u32x4& ov, const u32x4 (&yv)[KM]) {
+    constexpr bool CHK = decltype(chk_c)::value;
+    dots(chk_c, ov, yv);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j >= k || (CHK && !live[j])) continue;
+      dy[(size_t)sl[j] * row_vecs + c] = scaled(ov, gt[j]);
+    }
+  };
+  auto blk = [&](int b) {  // the row block visited at step b
+    const int p = b + sb;
+    return p >= nblk ? p - nblk : p;
   };
   // CHK: some choice of this token is dropped (rare); the common path has no
   // per-choice test in its loop
   auto walk = [&](auto chk_c) {
     constexpr bool CHK = decltype(chk_c)::value;
-    for (int b = 0; b < nblk; b += 2) {
-      const int p0 = b + sb < nblk ? b + sb : b + sb - nblk;
-      const int p1 = b + 1 + sb < nblk ? b + 1 + sb : b + 1 + sb - nblk;
-      const int c0 = p0 * kWave + lane;
-      const int c1 = b + 1 < nblk ? p1 * kWave + lane : row_vecs;
-      const bool ok0 = c0 < row_vecs, ok1 = c1 < row_vecs;  // the last block may be partial
-      u32x4 ov0 = {0, 0, 0, 0}, ov1 = {0, 0, 0, 0};
-      u32x4 yv0[KM], yv1[KM];
-      if (ok0) ov0 = __builtin_nontemporal_load(o + c0);
-      if (ok1) ov1 = __builtin_nontemporal_load(o + c1);
+    if constexpr (HOLD) {
+      // Reads and writes apart: y blocks interleaved with dy stores cost HBM
+      // read/write turnarounds, and dy does not depend on y.
+      u32x4 ov[kBwdHoldBlocks];
 #pragma unroll
-      for (int j = 0; j < KM; ++j)
-        if (j < k && (!CHK || live[j])) {
-          yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov0;
-          yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1) : ov1;
+      for (int b = 0; b < kBwdHoldBlocks; ++b) {
+        if (b >= nblk) break;  // uniform
+        const int c = blk(b) * kWave + lane;
+        ov[b] = c < row_vecs ? __builtin_nontemporal_load(o + c) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int b = 0; b < kBwdHoldBlocks; b += 2) {
+        if (b >= nblk) break;  // uniform
+        const int c0 = blk(b) * kWave + lane;
+        const int c1 = b + 1 < nblk ? blk(b + 1) * kWave + lane : row_vecs;
+        const bool ok0 = c0 < row_vecs, ok1 = c1 < row_vecs;
+        u32x4 yv0[KM], yv1[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k && (!CHK || live[j])) {
+            yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov[b];
+            yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1)
+                         : ov[b + 1];
+          }
+        if (ok0) dots(chk_c, ov[b], yv0);
+        if (ok1) dots(chk_c, ov[b + 1], yv1);
+        // One step's loads live at a time: its sums are complete (operands
+        // of the empty asm statements) before the next step's loads.
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k) asm volatile("" : "+v"(dot[j]));
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j >= k || (CHK && !live[j])) continue;
+        u32x4* const dr = dy + (size_t)sl[j] * row_vecs;
+#pragma unroll
+        for (int b = 0; b < kBwdHoldBlocks; ++b) {
+          if (b >= nblk) break;  // uniform
+          const int c = blk(b) * kWave + lane;
+          if (c < row_vecs) dr[c] = scaled(ov[b], gt[j]);
         }
-      if (ok0) block(chk_c, c0, ov0, yv0);
-      if (ok1) block(chk_c, c1, ov1, yv1);
+      }
+    } else {
+      for (int b = 0; b < nblk; b += 2) {
+        const int c0 = blk(b) * kWave + lane;
+        const int c1 = b + 1 < nblk ? blk(b + 1) * kWave + lane : row_vecs;
+        const bool ok0 = c0 < row_vecs, ok1 = c1 < row_vecs;  // the last block may be partial
+        u32x4 ov0 = {0, 0, 0, 0}, ov1 = {0, 0, 0, 0};
+        u32x4 yv0[KM], yv1[KM];
+        if (ok0) ov0 = __builtin_nontemporal_load(o + c0);
+        if (ok1) ov1 = __builtin_nontemporal_load(o + c1);
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < k && (!CHK || live[j])) {
+            yv0[j] = ok0 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c0) : ov0;
+            yv1[j] = ok1 ? __builtin_nontemporal_load(y + (size_t)sl[j] * row_vecs + c1) : ov1;
+          }
+        if (ok0) block(chk_c, c0, ov0, yv0);
+        if (ok1) block(chk_c, c1, ov1, yv1);
+      }
     }
   };
   bool all_live = true;
@@ -584,9 +656,14 @@ MOE_EXPORT moe_status moe_combine_bwd(const void* dout, const void* y, const int
   auto launch = [&](auto bf16_c, auto kk_c) {
     constexpr bool B = decltype(bf16_c)::value;
     constexpr int KV = decltype(kk_c)::value;
-    hipLaunchKernelGGL((combine_bwd_kernel<B, KV>), grid, block, 0, stream,
-                       static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
-                       gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
+    if (row_vecs <= kBwdHoldBlocks * kWave)
+      hipLaunchKernelGGL((combine_bwd_kernel<B, KV, true>), grid, block, 0, stream,
+                         static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
+                         gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
+    else
+      hipLaunchKernelGGL((combine_bwd_kernel<B, KV, false>), grid, block, 0, stream,
+                         static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y), slot_of,
+                         gates, T, k, row_vecs, static_cast<u32x4*>(dy), dgates);
   };
   auto by_k = [&](auto bf16_c) {
     switch (k) {

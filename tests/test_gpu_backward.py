@@ -72,7 +72,18 @@ STEP_CASES = [  # T, k, E, d, F, dtype, seed
 ]
 
 
-@pytest.mark.parametrize("T,k,E,d,F,dtype,seed", STEP_CASES)
+# Rows of several 1 KiB blocks for the combine kernels, which hold a row of at
+# most 8 KiB in registers and walk longer rows block by block: 5 blocks with
+# a partial last one (bf16 d 2368), 9 with a partial last one (bf16 d 4160,
+# fp32 d 2112), and k values with and without a k-specific kernel.
+LONG_ROW_CASES = [
+    (80, 6, 12, 2368, 64, "bf16", 5),
+    (96, 8, 16, 4160, 64, "bf16", 6),
+    (40, 3, 6, 2112, 64, "f32", 7),
+]
+
+
+@pytest.mark.parametrize("T,k,E,d,F,dtype,seed", STEP_CASES + LONG_ROW_CASES)
 def test_combine_and_route_bwd(T, k, E, d, F, dtype, seed):
     rng = np.random.default_rng(seed)
     S = T * k
@@ -95,6 +106,42 @@ def test_combine_and_route_bwd(T, k, E, d, F, dtype, seed):
     dx = ops.moe_dispatch_bwd(dev(da), dev(slot_of), T, k)
     torch.cuda.synchronize()
     assert_close("dx", host(dx), OB.dispatch_bwd(_w(da), slot_of, T, k), TAU[dtype])
+
+
+@pytest.mark.parametrize("T,k,E,d,F,dtype,seed", LONG_ROW_CASES + [(40, 8, 8, 4096, 64, "bf16", 8)])
+def test_combine_long_rows_with_dropped_choices(T, k, E, d, F, dtype, seed):
+    """The forward combine on rows of several 1 KiB blocks (held in registers
+    up to 8 KiB, exactly 8 blocks included; block by block beyond), with about
+    a tenth of the choices dropped (negative slot): a dropped choice is the
+    same as one pointing at an all-zero row."""
+    rng = np.random.default_rng(seed)
+    S = T * k
+    y = _store(rng.standard_normal((S, d)), dtype)
+    slot_of = rng.permutation(S).astype(np.int32)
+    drop = rng.random(S) < 0.1
+    drop[:k] = True                                       # token 0: every choice dropped
+    gates = rng.random((T, k)).astype(np.float32)
+    out = ops.moe_combine(dev(y), dev(np.where(drop, -1, slot_of).astype(np.int32)), dev(gates),
+                          T, k)
+    torch.cuda.synchronize()
+    y_z = np.vstack([_w(y), np.zeros((1, d))])
+    ref = oracle.combine(y_z, np.where(drop, S, slot_of).astype(np.int32),
+                         gates.astype(np.float64), T, k)
+    got = host(out)
+    assert not got[0].any()
+    assert_close("out", got, ref, TAU[dtype])
+    # the combine backward on the same layout: live slots get g dout, dropped
+    # choices get dgates 0 (the zero row's dot product)
+    dout = _store(rng.standard_normal((T, d)), dtype)
+    so_d = np.where(drop, -1, slot_of).astype(np.int32)
+    dy, dg = ops.moe_combine_bwd(dev(dout), dev(y), dev(so_d), dev(gates), T, k)
+    torch.cuda.synchronize()
+    g_z = np.where(drop.reshape(T, k), 0.0, gates.astype(np.float64))
+    ref_dy, ref_dg = OB.combine_bwd(_w(dout), y_z, np.where(drop, S, slot_of).astype(np.int32), g_z)
+    live = slot_of[~drop]
+    assert_close("dy", host(dy)[live], ref_dy[live], TAU[dtype])
+    assert_close("dgates", host(dg), ref_dg, 1e-4)
+    assert not host(dg)[0].any()
 
 
 @pytest.mark.parametrize("T,k,E,d,F,dtype,seed", STEP_CASES)
