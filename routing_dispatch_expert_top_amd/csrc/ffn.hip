@@ -702,7 +702,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     int kb, kt;  // weight gradients: first padded K column of B, K slices
   };
   auto decode = [&](int j) {
-    const int n = xcd * q + j;
+    const int n = j;  // global tile index
     if (WG) {
       const int pos = n / (MT * NT), rem = n - pos * MT * NT;
       Tile t{perm_row[pos], rem % NT, rem / NT, 0, 0, 0, 0};
@@ -934,14 +934,38 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   };
 
   // ---- the walk
-  int cur_j = blockIdx.x / kXcd;  // slot s: local tiles s, s + S, then claims
-  int nxt_j = cur_j + S;
+  // Tiles are global indices (-1: none). Slot s starts with its XCD's local
+  // tiles s and s + S, then claims.
+  auto own = [&](int l) { return l < qx ? xcd * q + l : -1; };
+  // The global tile of claim c on this XCD's counter. Forward launches of
+  // at least 8 tiles per workgroup: once the XCD's own tiles are all taken,
+  // thread 0 claims from the other XCDs' counters in turn (the XCDs run at
+  // different speeds, so equal shares end apart: up to 13% on a skewed
+  // load); every counter value is still taken by exactly one claim. With
+  // fewer tiles a stolen tile's lost L2 sharing and the serial claims cost
+  // more than the tail they save.
+  const bool steal = !WG && q >= 8 * S;
+  auto next_global = [&](int c) {
+    int gt = own(2 * S + c);
+    if constexpr (!WG) {
+      for (int i = 1; i < kXcd && gt < 0 && steal; ++i) {
+        const int x2 = (xcd + i) & (kXcd - 1);
+        const int q2 = min(q, total - x2 * q);
+        if (2 * S >= q2) continue;  // nothing that is claimed there
+        const int c2 = (int)atomicAdd(&queue[x2], 1u);
+        if (2 * S + c2 < q2) gt = x2 * q + 2 * S + c2;
+      }
+    }
+    return gt;
+  };
+  int cur_j = own(blockIdx.x / kXcd);
+  int nxt_j = own(blockIdx.x / kXcd + S);
   Tile cur{}, nxt{};
   int cm0 = 0, cm1 = 0, nm0 = 0, nm1 = 0;
   int nsrc = 0;
   int g = 0;  // ring slot of the current tile's slice 0
   const char* b_base = nullptr;
-  if (cur_j < qx) {
+  if (cur_j >= 0) {
     cur = decode(cur_j);
     tile_rows(cur, cm0, cm1);
     set_boff(cur.nt * Cfg::kOutCols);
@@ -957,8 +981,8 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     }
   }
   int pend_st = 0;  // store instructions of the previous epilogue (per thread, uniform)
-  while (cur_j < qx) {
-    const bool has_next = nxt_j < qx;  // uniform
+  while (cur_j >= 0) {
+    const bool has_next = nxt_j >= 0;  // uniform
     int claim = 0;
     if (has_next) {
       nxt = decode(nxt_j);
@@ -1155,7 +1179,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       int claimed = 0, kt_n = 0;
       if (has_next) {
         // hand the claim (tile i+2) to every wave before the ring is refilled
-        if (tid == 0) *reinterpret_cast<int*>(rb) = claim_s;
+        if (tid == 0) *reinterpret_cast<int*>(rb) = next_global(claim_s);
         wg_barrier();
         claimed = *reinterpret_cast<const int*>(rb);
         MOE_WAIT_LGKM0();
@@ -1225,7 +1249,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
       cm1 = nm1;
       KT = kt_n;
       cur_j = nxt_j;
-      nxt_j = 2 * S + __builtin_amdgcn_readfirstlane(claimed);
+      nxt_j = __builtin_amdgcn_readfirstlane(claimed);
       continue;
     }
     if (has_next) {
@@ -1381,7 +1405,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     if (!has_next) break;  // uniform
     // hand the claim (tile i+2) to every wave through region 0, then move on
     wg_barrier();  // every staged row has been read
-    if (tid == 0) *reinterpret_cast<int*>(ring_b + rgn0) = claim_s;
+    if (tid == 0) *reinterpret_cast<int*>(ring_b + rgn0) = next_global(claim_s);
     wg_barrier();
     const int claimed = *reinterpret_cast<const int*>(ring_b + rgn0);  // read before the next
     // tile's slice 0 barrier, after which its A(1) DMA may overwrite region 0
@@ -1389,7 +1413,7 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
     cm0 = nm0;
     cm1 = nm1;
     cur_j = nxt_j;
-    nxt_j = 2 * S + __builtin_amdgcn_readfirstlane(claimed);
+    nxt_j = __builtin_amdgcn_readfirstlane(claimed);
   }
   // The last workgroup to finish leaves the queue zeroed for the next
   // launch. Every workgroup's claims have returned (their values were used)
