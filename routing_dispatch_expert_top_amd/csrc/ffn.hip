@@ -937,24 +937,22 @@ __global__ __launch_bounds__(256) void ffn_persistent_kernel(
   // Tiles are global indices (-1: none). Slot s starts with its XCD's local
   // tiles s and s + S, then claims.
   auto own = [&](int l) { return l < qx ? xcd * q + l : -1; };
-  // The global tile of claim c on this XCD's counter. Forward launches of
-  // at least 8 tiles per workgroup: once the XCD's own tiles are all taken,
+  // The global tile of claim c on this XCD's counter. Launches of at least
+  // 8 tiles per workgroup: once the XCD's own tiles are all taken,
   // thread 0 claims from the other XCDs' counters in turn (the XCDs run at
   // different speeds, so equal shares end apart: up to 13% on a skewed
   // load); every counter value is still taken by exactly one claim. With
   // fewer tiles a stolen tile's lost L2 sharing and the serial claims cost
   // more than the tail they save.
-  const bool steal = !WG && q >= 8 * S;
+  const bool steal = q >= 8 * S;
   auto next_global = [&](int c) {
     int gt = own(2 * S + c);
-    if constexpr (!WG) {
-      for (int i = 1; i < kXcd && gt < 0 && steal; ++i) {
-        const int x2 = (xcd + i) & (kXcd - 1);
-        const int q2 = min(q, total - x2 * q);
-        if (2 * S >= q2) continue;  // nothing that is claimed there
-        const int c2 = (int)atomicAdd(&queue[x2], 1u);
-        if (2 * S + c2 < q2) gt = x2 * q + 2 * S + c2;
-      }
+    for (int i = 1; i < kXcd && gt < 0 && steal; ++i) {
+      const int x2 = (xcd + i) & (kXcd - 1);
+      const int q2 = min(q, total - x2 * q);
+      if (2 * S >= q2) continue;  // nothing that is claimed there
+      const int c2 = (int)atomicAdd(&queue[x2], 1u);
+      if (2 * S + c2 < q2) gt = x2 * q + 2 * S + c2;
     }
     return gt;
   };
