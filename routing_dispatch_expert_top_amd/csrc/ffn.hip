@@ -21,7 +21,8 @@
 // walks its XCD's share of the tile list in order, claiming tiles from a
 // per-XCD counter in the caller's workspace, so that the tiles running at
 // once on an XCD are neighbours that share weight panels and activation
-// tiles in its L2. The same kernel, in a weight-gradient mode, computes the
+// tiles in its L2 (at the end, workgroups of an XCD that is done take the
+// other XCDs' remaining tiles). The same kernel, in a weight-gradient mode, computes the
 // backward's weight gradients; a one-tile-per-workgroup kernel computes its
 // data gradients.
 //
@@ -606,7 +607,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void dgrad_bf16_kernel(
 // Tiles are handed out in order, per XCD: XCD x owns logical tiles
 // [x q, (x+1) q) (the order of decode_tile, q = ceil(tiles / 8)); its
 // workgroups take local tiles s and s + S first (S workgroups per XCD, slot
-// s), then claim the next one from the XCD's counter. Tiles running at one
+// s), then claim the next one from the XCD's counter (and, in launches of
+// at least 8 tiles per workgroup, from the other XCDs' counters once their
+// own is exhausted). Tiles running at one
 // moment on an XCD therefore stay a window of neighbouring tiles that share
 // weight panels and activation tiles in that XCD's L2 (a static walk lets
 // workgroups drift apart and lose that sharing). A claim is made two tiles
