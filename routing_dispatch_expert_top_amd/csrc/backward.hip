@@ -265,35 +265,25 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict_
 
 // ---------------------------------------------------------------- padded transposes
 
-// One min step against the lane the DPP control CTRL names, on both 32-bit
-// halves of a 64-bit key.
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_min_step(uint64_t x) {
-  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
-  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
-  const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)phi << 32) | plo;
-  return o < x ? o : x;
-}
-
 // kseg[e] = sum over e' < e of ceil(M_e' / 64) * 64 (each expert's slot count
 // rounded up to whole 64-wide K slices), kseg[E] = the padded total.
 // eorder[8 * cap] (cap = ceil(E / 8)): the experts in the order the
 // weight-gradient GEMM walks them. Its tiles go to the 8 XCDs in 8
 // contiguous ranges of cap experts each, and a tile's work grows with its
-// expert's slot count, so the experts are dealt longest first to the
-// least-loaded XCD range with room left (ties: lower range); unused
-// positions hold -1. It also clears the weight-gradient launch's tile queue.
+// expert's slot count, so the experts are dealt longest first (ties: lower
+// expert) to the ranges in turn: rank r to range r mod 8, position r / 8;
+// unused positions hold -1. What imbalance is left, the launch evens out by
+// claiming across XCDs at its end. (A serial least-loaded greedy over the
+// ranks balanced a little better but took about 25 us of one wavefront.)
+// It also clears the weight-gradient launch's tile queue.
 __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ expert_off,
                                                           int E, int32_t* __restrict__ kseg,
                                                           int32_t* __restrict__ eorder,
                                                           uint32_t* __restrict__ queue) {
   if (threadIdx.x < kQueueWords) queue[threadIdx.x] = 0u;
   __shared__ Sched sc;
-  __shared__ int32_t sorted[kMaxE];
-  __shared__ int32_t slen[kMaxE];
   build_schedule(sc, expert_off, E, 64);
-  const int e = threadIdx.x;
+  const int e = threadIdx.x, cap = (E + 7) / 8;
   for (int i = threadIdx.x; i <= E; i += blockDim.x) kseg[i] = sc.mt_off[i] * 64;
   if (e < E) {  // rank by padded length, longest first (ties: lower expert)
     const int my = sc.mt_off[e + 1] - sc.mt_off[e];
@@ -302,49 +292,9 @@ __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restr
       const int len = sc.mt_off[f + 1] - sc.mt_off[f];
       rank += len > my || (len == my && f < e);
     }
-    sorted[rank] = e;
-    slen[rank] = my;
+    eorder[(rank % 8) * cap + rank / 8] = e;  // longest first, dealt to the ranges in turn
   }
-  __syncthreads();
-  if (threadIdx.x >= kWave) return;
-  // One wavefront runs the greedy. Lane l holds sorted positions l + 64 i
-  // (step r reads its expert and length from lane r mod 64), lanes 0..7 hold
-  // one XCD range each, and the least-loaded range is an 8-lane minimum of
-  // (load, range) keys by DPP moves inside each group of 8 lanes.
-  const int cap = (E + 7) / 8, lane = threadIdx.x;
-  constexpr int kPer = kMaxE / kWave;
-  int sx[kPer], sn[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int r = lane + kWave * i;
-    sx[i] = r < E ? sorted[r] : -1;
-    sn[i] = r < E ? slen[r] : 0;
-  }
-  uint64_t load = 0;  // lanes 0..7: one XCD range each
-  int count = 0;
-  for (int r = 0; r < E; ++r) {
-    int xv = sx[0], nv = sn[0];
-#pragma unroll
-    for (int i = 1; i < kPer; ++i)
-      if (r / kWave == i) {
-        xv = sx[i];
-        nv = sn[i];
-      }
-    const int x = __builtin_amdgcn_readlane(xv, r % kWave);
-    const int len = __builtin_amdgcn_readlane(nv, r % kWave);
-    uint64_t key = (lane < 8 && count < cap) ? (load << 8) | (uint64_t)lane : ~0ull;
-    key = dpp_min_step<0xB1>(key);   // quad_perm [1,0,3,2]
-    key = dpp_min_step<0x4E>(key);   // quad_perm [2,3,0,1]
-    key = dpp_min_step<0x141>(key);  // row_half_mirror: the 8-lane minimum
-    const int b = __builtin_amdgcn_readlane((int)(uint32_t)key, 0) & 0xFF;  // least-loaded range
-    if (lane == b) {
-      eorder[b * cap + count] = x;
-      load += (uint64_t)len;
-      ++count;
-    }
-  }
-  if (lane < 8)
-    for (int i = count; i < cap; ++i) eorder[lane * cap + i] = -1;  // each lane its own range
+  for (int r = E + (int)threadIdx.x; r < 8 * cap; r += blockDim.x) eorder[(r % 8) * cap + r / 8] = -1;
 }
 
 // dst [W][ldk] (bf16): dst[w][kseg[e] + j] = src[row(s)][w] for slot s =
